@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Throughput of the low-precision GEMM on one MI355X.
+
+A step is one GEMM over one batch of synthetic inputs already resident in
+HBM.  The headline workload is the INT8 square GEMM at M = N = K = 8192 (A
+row-major, B K-contiguous, int32 C); the INT4 and FP16 GEMMs at 8192 are timed
+in the same run and reported under "also".  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload i8-8192]
+                    [--also i4-8192,f16-8192] [--cpu-seconds S]
+
+Timing: W untimed launches, then K launches on the current stream bracketed by
+device synchronisations; ms_per_step is the whole timed region / K, and the
+roofline uses the average kernel duration from an event pair around each
+launch on that same stream.  The output of the last timed launch is checked
+against the CPU oracle on sampled rows.  For the HBM-bound LLM shapes the
+weight operand rotates over enough copies (>= 336 MiB) that the 256 MiB
+Infinity Cache cannot hold them.
+
+cpu_baseline: the CPU oracle (plain OpenMP loops) timed on this host on a
+bounded sample of the headline workload (a subset of output rows, sized to
+about --cpu-seconds of work), scaled to the metric's unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "INT8/INT4 TOPS and FP16 TFLOPS at N=8192 on 1 MI355X; % of MFMA peak"
+# Dense MFMA peaks of the MI355X (256 CUs, 2.4 GHz): int8 8192 ops and fp16
+# 4096 flops per CU per clock.  INT4 runs on the int8 MFMA.
+PEAK_TOPS = {"i8": 5033.2, "i4": 5033.2, "dq": 5033.2, "f16": 2516.6}
+HBM_PEAK_GBS = 8000.0
+UNIT = {"i8": "TOPS", "i4": "TOPS", "dq": "TOPS", "f16": "TFLOPS"}
+DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "f16": "f16"}
+KERNEL_SOURCES = ["precision_dense_gemm_02_amd/csrc/gemm_kernels.hpp",
+                  "precision_dense_gemm_02_amd/csrc/lpgemm.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse_workload(name: str):
+    kind, size = name.split("-")
+    size = int(size)
+    if kind == "llm":
+        from precision_dense_gemm_02_amd import inputs
+        return "dq", size, inputs.LLM_N, inputs.LLM_K
+    if kind not in ("i8", "i4", "f16"):
+        raise SystemExit(f"unknown workload {name}")
+    return kind, size, size, size
+
+
+class Workload:
+    """Inputs on the device and a closure that launches one GEMM."""
+
+    def __init__(self, name: str):
+        import numpy as np
+        import torch
+
+        import precision_dense_gemm_02_amd as lp
+        from precision_dense_gemm_02_amd import inputs
+
+        self.name = name
+        self.kind, M, N, K = parse_workload(name)
+        self.M, self.N, self.K = M, N, K
+        dev = torch.device("cuda:0")
+
+        def to(x):
+            return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+        kind = self.kind
+        if kind == "i8":
+            self.seed = inputs.seed_for("i8", M)
+            p = inputs.int8_problem(M, N, K, self.seed)
+            self.host = p
+            a, b = to(p.a), to(p.b_t)
+            out = torch.empty((M, N), dtype=torch.int32, device=dev)
+            self.launch = lambda i: lp.gemm_i8(a, b, out=out)
+            self.in_bytes = M * K + N * K
+            self.out_bytes = 4 * M * N
+        elif kind == "i4":
+            self.seed = inputs.seed_for("i4", M)
+            p = inputs.int4_problem(M, N, K, self.seed)
+            self.host = p
+            a, b = to(p.a_packed), to(p.b_packed)
+            out = torch.empty((M, N), dtype=torch.int32, device=dev)
+            self.launch = lambda i: lp.gemm_i4(a, b, K, out=out)
+            self.in_bytes = (M * K + N * K) // 2
+            self.out_bytes = 4 * M * N
+        elif kind == "f16":
+            self.seed = inputs.seed_for("f16", M)
+            p = inputs.f16_problem(M, N, K, self.seed)
+            self.host = p
+            a, b = to(p.a), to(p.b_t)
+            out = torch.empty((M, N), dtype=torch.float32, device=dev)
+            self.launch = lambda i: lp.gemm_f16(a, b, out=out)
+            self.in_bytes = 2 * (M * K + N * K)
+            self.out_bytes = 4 * M * N
+        else:  # dequantised LLM projection
+            self.seed = inputs.seed_for("llm", M)
+            p = inputs.llm_problem(M, self.seed)
+            self.host = p
+            a, rs, cs = to(p.a), to(p.row_scale), to(p.col_scale)
+            # rotate weight copies so that the timed launches stream B from HBM
+            copies = max(1, -(-336 * 2 ** 20 // (N * K)))
+            bs = [to(p.b_t)] + [to(p.b_t) for _ in range(copies - 1)]
+            out = torch.empty((M, N), dtype=torch.float32, device=dev)
+            self.launch = lambda i: lp.gemm_i8_dequant(a, bs[i % len(bs)], rs, cs, out=out)
+            self.in_bytes = M * K + N * K + 4 * (M + N)
+            self.out_bytes = 4 * M * N
+        self.out = out
+        self.ops = 2 * M * N * K
+
+    def check_sampled(self, nrows: int = 8) -> str:
+        """Compare sampled rows of the last output with the CPU oracle."""
+        import numpy as np
+
+        import oracle
+        rng = np.random.default_rng(123)
+        rows = sorted(set([0, self.M - 1] + rng.choice(self.M, min(nrows, self.M), replace=False).tolist()))
+        got = self.out.cpu().numpy()[rows]
+        p = self.host
+        if self.kind == "i8":
+            ok = np.array_equal(got, oracle.gemm_i8(p.a, p.b_t, rows=rows))
+        elif self.kind == "i4":
+            ok = np.array_equal(got, oracle.gemm_i4(p.a_packed, p.b_packed, self.K, rows=rows))
+        elif self.kind == "f16":
+            ref, den = oracle.gemm_f16(p.a, p.b_t, rows=rows)
+            e = oracle.f16_rel_error(got, ref, den)
+            return f"max_rel_err {e['max_rel']:.3e} over {len(rows)} rows (tol 1e-3)" \
+                if e["max_rel"] <= 1e-3 else f"FAIL max_rel_err {e['max_rel']:.3e}"
+        else:
+            ref = oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale, rows=rows)
+            ok = np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+        return f"bit-exact over {len(rows)} sampled rows" if ok else "FAIL"
+
+
+def time_workload(w: Workload, steps: int, warmup: int) -> dict:
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        w.launch(i)
+    torch.cuda.synchronize()
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    torch.cuda.synchronize()
+    region0.record(stream)
+    for i in range(steps):
+        pairs[i][0].record(stream)
+        w.launch(i)
+        pairs[i][1].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = region0.elapsed_time(region1)
+    per = sorted(a.elapsed_time(b) for a, b in pairs)
+    return {"ms_per_step": total_ms / steps,
+            "kernel_ms_avg": sum(per) / len(per),
+            "kernel_ms_min": per[0],
+            "kernel_ms_median": per[len(per) // 2]}
+
+
+def roofline(w: Workload, t: dict) -> dict:
+    kind = w.kind
+    alg_bytes = w.in_bytes + w.out_bytes
+    sec = t["kernel_ms_avg"] / 1e3
+    intensity = w.ops / alg_bytes
+    ridge = PEAK_TOPS[kind] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(w.name)
+        if rec and rec.get("kernel_source_hash") == kernel_source_hash():
+            traffic = rec["fetch_bytes"] + rec["write_bytes"]
+    except (OSError, ValueError):
+        traffic = None
+    if intensity >= ridge:
+        achieved = w.ops / sec / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TOPS[kind],
+                "unit": "TFLOP/s" if kind == "f16" else "TOP/s",
+                "frac": round(achieved / PEAK_TOPS[kind], 4), "traffic": traffic,
+                "algorithmic_bytes": alg_bytes, "ops_per_launch": w.ops}
+    achieved = alg_bytes / sec / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes": alg_bytes, "ops_per_launch": w.ops}
+
+
+def cpu_baseline(w: Workload, seconds: float) -> dict:
+    """The oracle timed on this host on a bounded set of output rows."""
+    import oracle
+    p = w.host
+    threads = oracle.num_threads()
+
+    def run(rows):
+        t0 = time.perf_counter()
+        if w.kind == "i8":
+            oracle.gemm_i8(p.a, p.b_t, rows=rows)
+        elif w.kind == "i4":
+            oracle.gemm_i4(p.a_packed, p.b_packed, w.K, rows=rows)
+        elif w.kind == "f16":
+            oracle.gemm_f16(p.a, p.b_t, rows=rows)
+        else:
+            oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale, rows=rows)
+        return time.perf_counter() - t0
+
+    probe_rows = min(w.M, threads)
+    t_probe = run(range(probe_rows))
+    per_row = t_probe / probe_rows
+    nrows = int(min(w.M, max(threads, seconds / max(per_row, 1e-9))))
+    nrows = max(threads, (nrows // threads) * threads) if nrows >= threads else nrows
+    nrows = min(nrows, w.M)
+    t = run(range(nrows))
+    ops = 2 * nrows * w.N * w.K
+    return {"value": round(ops / t / 1e12, 6), "unit": UNIT[w.kind], "cores": threads,
+            "kind": "oracle", "seconds": round(t, 2),
+            "sample": f"rows 0..{nrows - 1} of the {w.M}x{w.N}x{w.K} {w.kind} product "
+                      f"({nrows * w.N} outputs)"}
+
+
+def measure(name: str, steps: int, warmup: int) -> tuple:
+    w = Workload(name)
+    t = time_workload(w, steps, warmup)
+    r = roofline(w, t)
+    value = w.ops / (t["ms_per_step"] / 1e3) / 1e12
+    rec = {"workload": name, "value": round(value, 1), "unit": UNIT[w.kind],
+           "ms_per_step": round(t["ms_per_step"], 5),
+           "kernel_ms_avg": round(t["kernel_ms_avg"], 5),
+           "kernel_ms_min": round(t["kernel_ms_min"], 5),
+           "pct_mfma_peak": round(100 * value / PEAK_TOPS[w.kind], 2),
+           "roofline": r, "parity": w.check_sampled()}
+    return w, rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="i8-8192")
+    ap.add_argument("--also", default="i4-8192,f16-8192",
+                    help="comma-separated extra workloads timed in the same run ('' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import precision_dense_gemm_02_amd as lp
+    lp.load_library()
+
+    w, head = measure(args.workload, args.steps, args.warmup)
+    print(f"# {head['workload']}: {head['value']} {head['unit']} ({head['parity']})",
+          file=sys.stderr, flush=True)
+    also = []
+    for name in [s for s in args.also.split(",") if s and s != args.workload]:
+        _, rec = measure(name, args.steps, args.warmup)
+        print(f"# {rec['workload']}: {rec['value']} {rec['unit']} ({rec['parity']})",
+              file=sys.stderr, flush=True)
+        also.append(rec)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        print(f"# cpu oracle: {cpu['value']} {cpu['unit']} on {cpu['cores']} threads",
+              file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE[w.kind], "data": "synthetic",
+        "config": {"workload": head["workload"], "M": w.M, "N": w.N, "K": w.K, "seed": w.seed,
+                   "layout": "A row-major, B K-contiguous, C row-major"},
+        "pct_mfma_peak": head["pct_mfma_peak"],
+        "kernel_ms_avg": head["kernel_ms_avg"],
+        "parity": head["parity"],
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "also": also,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,123 @@
+/*
+ * lpgemm: low-precision dense GEMM C = A.B for one AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one the PTX-vs-WMMA summary page (thecoregrid.dev,
+ * "PTX Tensor-Core GEMM", paragraphs on FP16, INT8 and INT4 and on the s4 mma
+ * shape) measures: a dense GEMM in FP16, INT8 and INT4.  Integer operands are
+ * summed exactly in int32; FP16 operands are summed in FP32.  A fourth entry
+ * point applies a per-row x per-column fp32 dequantisation to the exact int8
+ * product, the step after the GEMM in quantised-LLM inference (the page's
+ * closing recommendation on quantised LLM inference on one GPU).
+ *
+ * Layouts (fixed; there are no leading-dimension arguments):
+ *   A  M x K, row-major (each row is K contiguous elements).
+ *   B  K x N stored K-contiguous: N rows of K contiguous elements, i.e. the
+ *      N x K row-major array B^T (the layout the page's ablation keeps;
+ *      its variant with B transposed lost coalescing).
+ *   C  M x N, row-major.
+ *   INT4: two signed 4-bit values per byte along k; byte t of a row holds
+ *      element 2t in its low nibble and element 2t+1 in its high nibble, each
+ *      a two's-complement nibble (-8..7).  A_packed is M x K/2 bytes and
+ *      B_packed is N x K/2 bytes.
+ *   FP16: IEEE binary16 (bit-compatible with _Float16 / torch.float16).
+ *   Scales: row_scale[M] and col_scale[N], fp32.
+ *
+ * Semantics: C is overwritten with A.B (no alpha/beta, no accumulation into
+ * C).  The work is enqueued on `stream` (NULL = the default stream) and the
+ * call returns after the enqueue, without synchronising.
+ *
+ * Ownership: every pointer is device memory owned by the caller, which must
+ * keep it valid until the enqueued work completes.  The library allocates no
+ * memory, keeps no per-call state and may be called from several host threads.
+ * C must not overlap A, B or the scales.
+ *
+ * Degenerate sizes: M = 0 or N = 0 is an empty product; the call returns
+ * LPGEMM_SUCCESS without enqueueing anything or reading any pointer.  K = 0
+ * is an empty sum: C is filled with zeros, and A and B may then be NULL.
+ *
+ * Errors (checked on the host before any HIP call, in this order):
+ *   LPGEMM_ERROR_INVALID_VALUE     M, N or K negative, or M or N above
+ *                                  2^31 - 1.
+ *   LPGEMM_ERROR_UNSUPPORTED_SHAPE K breaks the entry point's divisibility or
+ *                                  range rule (each function says which).
+ *   (M = 0 or N = 0 returns LPGEMM_SUCCESS here.)
+ *   LPGEMM_ERROR_INVALID_VALUE     C, a scale array, or (for K > 0) A or B
+ *                                  is NULL.
+ *   LPGEMM_ERROR_MISALIGNED        A, B or C not 16-byte aligned (the scale
+ *                                  arrays need only 4-byte alignment).
+ * then, after selecting the current device:
+ *   LPGEMM_ERROR_ARCH              the current device is not gfx950, or its
+ *                                  properties could not be read.
+ *   LPGEMM_ERROR_LAUNCH            the kernel launch was rejected.
+ * Faults during execution are reported by the caller's next synchronisation
+ * of the stream, as for any HIP kernel.  M and N need no divisibility: edge
+ * tiles are masked.
+ */
+#ifndef LPGEMM_H
+#define LPGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's own hipStream_t. */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum lpgemm_status {
+    LPGEMM_SUCCESS = 0,
+    LPGEMM_ERROR_INVALID_VALUE = 1,
+    LPGEMM_ERROR_MISALIGNED = 2,
+    LPGEMM_ERROR_UNSUPPORTED_SHAPE = 3,
+    LPGEMM_ERROR_ARCH = 4,
+    LPGEMM_ERROR_LAUNCH = 5
+} lpgemm_status;
+
+/* Largest K of the integer entry points: with every product equal to
+ * (-128)^2 = 2^14, the exact sum 2^14 * K still fits int32 for K <= 131071. */
+#define LPGEMM_MAX_K_INT 131071
+/* Largest K of the fp16 entry point: an operand panel of 256 rows then stays
+ * well below 2 GiB, the reach of the 32-bit offsets the kernels' loads use. */
+#define LPGEMM_MAX_K_F16 1048576
+
+/* INT8: C[i][j] = sum_k A[i][k] * B[k][j], exact in int32.
+ * A: M x K int8, B: N x K int8 (K-contiguous), C: M x N int32.
+ * K must be a multiple of 16 and at most LPGEMM_MAX_K_INT. */
+lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, const int8_t *B,
+                        int32_t *C, hipStream_t stream);
+
+/* INT4: the same exact int32 product over signed 4-bit operands packed two
+ * per byte (low nibble = even k).  A_packed: M x K/2 bytes, B_packed: N x K/2
+ * bytes, C: M x N int32.  K counts 4-bit elements; it must be a multiple of
+ * 32 and at most LPGEMM_MAX_K_INT. */
+lpgemm_status lpgemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A_packed,
+                        const uint8_t *B_packed, int32_t *C, hipStream_t stream);
+
+/* FP16: C[i][j] = sum_k A[i][k] * B[k][j] with binary16 operands, products
+ * and sums in binary32 (the summation order is unspecified).  A: M x K,
+ * B: N x K (K-contiguous), C: M x N fp32.  The pointers have the bit layout of
+ * binary16 (_Float16 or uint16_t storage).  K must be a multiple of 8 and at
+ * most LPGEMM_MAX_K_F16. */
+lpgemm_status lpgemm_f16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                         float *C, hipStream_t stream);
+
+/* INT8 with dequantisation: acc = the exact int32 product of lpgemm_i8, then
+ * C[i][j] = ((float)acc * row_scale[i]) * col_scale[j], each multiplication
+ * rounded to binary32 (nearest even) in that order.  C: M x N fp32.
+ * K as for lpgemm_i8. */
+lpgemm_status lpgemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A,
+                                const int8_t *B, const float *row_scale,
+                                const float *col_scale, float *C, hipStream_t stream);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char *lpgemm_status_string(lpgemm_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int lpgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LPGEMM_H */

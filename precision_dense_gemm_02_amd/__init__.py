@@ -1,0 +1,13 @@
+"""Low-precision dense GEMM for AMD MI355X (gfx950).
+
+C = A . B with INT8 and packed INT4 operands summed exactly in int32, FP16
+operands summed in FP32, and an INT8 variant with per-row x per-column fp32
+dequantisation.  The work runs in hand-written HIP kernels behind the C ABI of
+include/lpgemm.h; this package is the torch-facing binding (see _binding.py),
+the in-tree build step (build.py) and the seeded input generators (inputs.py).
+"""
+from ._binding import (LpgemmError, gemm_f16, gemm_i4, gemm_i8, gemm_i8_dequant,  # noqa: F401
+                       load_library, status_string, version)
+
+__all__ = ["LpgemmError", "gemm_i8", "gemm_i4", "gemm_f16", "gemm_i8_dequant",
+           "load_library", "status_string", "version"]

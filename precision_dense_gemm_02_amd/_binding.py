@@ -1,0 +1,211 @@
+"""ctypes binding of liblpgemm.so, the C ABI declared in include/lpgemm.h.
+
+Argument marshalling only: every function checks the torch tensors it is
+given (dtype, shape, contiguity, device), allocates the output with torch when
+none is passed, and calls the library entry point of the same name on the
+current torch stream.  All arithmetic runs in the library's HIP kernels.  If
+the library has not been built the first call raises -- there is no other
+implementation to fall back on.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblpgemm.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "lpgemm.h")
+
+LPGEMM_SUCCESS = 0
+LPGEMM_ERROR_INVALID_VALUE = 1
+LPGEMM_ERROR_MISALIGNED = 2
+LPGEMM_ERROR_UNSUPPORTED_SHAPE = 3
+LPGEMM_ERROR_ARCH = 4
+LPGEMM_ERROR_LAUNCH = 5
+
+MAX_K_INT = 131071
+MAX_K_F16 = 1048576
+
+
+class LpgemmError(RuntimeError):
+    """A non-success status from the library."""
+
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = status_string(status)
+        super().__init__(f"{what}: {msg} (status {status})" if what else f"{msg} (status {status})")
+
+
+_lib = None
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def load_library():
+    """Load liblpgemm.so (once) and declare the entry points' signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing; build it with "
+                "`python -m precision_dense_gemm_02_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name in ("lpgemm_i8", "lpgemm_i4", "lpgemm_f16"):
+            f = getattr(lib, name)
+            f.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p]
+            f.restype = ctypes.c_int
+        lib.lpgemm_i8_dequant.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p]
+        lib.lpgemm_i8_dequant.restype = ctypes.c_int
+        lib.lpgemm_status_string.argtypes = [ctypes.c_int]
+        lib.lpgemm_status_string.restype = ctypes.c_char_p
+        lib.lpgemm_version.argtypes = []
+        lib.lpgemm_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def declared_functions() -> list:
+    """Names of the functions include/lpgemm.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(lpgemm_\w+)\s*\(", text, flags=re.M)
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().lpgemm_status_string(int(status)).decode()
+    except RuntimeError:
+        return f"status {status}"
+
+
+def version() -> int:
+    return int(load_library().lpgemm_version())
+
+
+def _check(status: int, what: str) -> None:
+    if status != LPGEMM_SUCCESS:
+        raise LpgemmError(status, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _operand(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _output(out, shape, dtype, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if out.dtype != dtype or tuple(out.shape) != tuple(shape) or out.device != device \
+            or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {dtype} tensor of shape {shape} on {device}")
+    return out
+
+
+def _same_device(*ts):
+    d = ts[0].device
+    for t in ts[1:]:
+        if t.device != d:
+            raise ValueError("all tensors must be on the same device")
+    return d
+
+
+def gemm_i8(a, b_t, out=None):
+    """int32 C = A . B; a: M x K int8, b_t: N x K int8 (B stored K-contiguous)."""
+    torch = _torch()
+    _operand(a, torch.int8, "a")
+    _operand(b_t, torch.int8, "b_t")
+    if a.shape[1] != b_t.shape[1]:
+        raise ValueError(f"K mismatch: a {tuple(a.shape)}, b_t {tuple(b_t.shape)}")
+    dev = _same_device(a, b_t)
+    M, K = a.shape
+    N = b_t.shape[0]
+    out = _output(out, (M, N), torch.int32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_i8(M, N, K, a.data_ptr(), b_t.data_ptr(), out.data_ptr(),
+                                        _stream_handle(dev)), "lpgemm_i8")
+    return out
+
+
+def gemm_i4(a_packed, b_packed, K: Optional[int] = None, out=None):
+    """int32 C = A . B over signed int4 packed two per byte along k (low nibble
+    = even k); a_packed: M x K/2 uint8, b_packed: N x K/2 uint8."""
+    torch = _torch()
+    _operand(a_packed, torch.uint8, "a_packed")
+    _operand(b_packed, torch.uint8, "b_packed")
+    if a_packed.shape[1] != b_packed.shape[1]:
+        raise ValueError("packed K mismatch")
+    if K is None:
+        K = 2 * a_packed.shape[1]
+    if 2 * a_packed.shape[1] != K:
+        raise ValueError(f"K={K} does not match packed width {a_packed.shape[1]}")
+    dev = _same_device(a_packed, b_packed)
+    M = a_packed.shape[0]
+    N = b_packed.shape[0]
+    out = _output(out, (M, N), torch.int32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_i4(M, N, K, a_packed.data_ptr(), b_packed.data_ptr(),
+                                        out.data_ptr(), _stream_handle(dev)), "lpgemm_i4")
+    return out
+
+
+def gemm_f16(a, b_t, out=None):
+    """fp32 C = A . B; a: M x K fp16, b_t: N x K fp16 (B stored K-contiguous)."""
+    torch = _torch()
+    _operand(a, torch.float16, "a")
+    _operand(b_t, torch.float16, "b_t")
+    if a.shape[1] != b_t.shape[1]:
+        raise ValueError(f"K mismatch: a {tuple(a.shape)}, b_t {tuple(b_t.shape)}")
+    dev = _same_device(a, b_t)
+    M, K = a.shape
+    N = b_t.shape[0]
+    out = _output(out, (M, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_f16(M, N, K, a.data_ptr(), b_t.data_ptr(), out.data_ptr(),
+                                         _stream_handle(dev)), "lpgemm_f16")
+    return out
+
+
+def gemm_i8_dequant(a, b_t, row_scale, col_scale, out=None):
+    """fp32 C = ((float)(A . B) * row_scale[i]) * col_scale[j]."""
+    torch = _torch()
+    _operand(a, torch.int8, "a")
+    _operand(b_t, torch.int8, "b_t")
+    if a.shape[1] != b_t.shape[1]:
+        raise ValueError(f"K mismatch: a {tuple(a.shape)}, b_t {tuple(b_t.shape)}")
+    M, K = a.shape
+    N = b_t.shape[0]
+    for t, n, name in ((row_scale, M, "row_scale"), (col_scale, N, "col_scale")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 1 \
+                or t.shape[0] != n or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 GPU vector of length {n}")
+    dev = _same_device(a, b_t, row_scale, col_scale)
+    out = _output(out, (M, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_i8_dequant(M, N, K, a.data_ptr(), b_t.data_ptr(),
+                                                row_scale.data_ptr(), col_scale.data_ptr(),
+                                                out.data_ptr(), _stream_handle(dev)),
+               "lpgemm_i8_dequant")
+    return out

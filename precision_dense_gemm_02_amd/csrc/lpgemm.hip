@@ -1,0 +1,182 @@
+// Host side of liblpgemm: the C-ABI entry points declared in include/lpgemm.h.
+//
+// Each call validates its arguments on the host (no HIP call before that),
+// checks once per device that the device is gfx950, picks a tile
+// configuration for the shape, and enqueues one kernel on the caller's
+// stream.  Nothing is allocated and no state is kept between calls apart from
+// the per-device property cache.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/lpgemm.h"
+#include "gemm_kernels.hpp"
+
+namespace lpgemm {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  bool probed = false;
+  bool is_gfx950 = false;
+  int cu_count = 0;
+};
+
+std::mutex g_device_mutex;
+DeviceInfo g_devices[kMaxDevices];
+
+// Current device's properties, read once per device.
+lpgemm_status current_device(DeviceInfo& out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERROR_ARCH;
+  std::lock_guard<std::mutex> lock(g_device_mutex);
+  DeviceInfo& d = g_devices[dev];
+  if (!d.probed) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LPGEMM_ERROR_ARCH;
+    d.is_gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cu_count = prop.multiProcessorCount;
+    d.probed = true;
+  }
+  out = d;
+  return d.is_gfx950 ? LPGEMM_SUCCESS : LPGEMM_ERROR_ARCH;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Host-only argument checks, in the order the header documents.  Sets
+// `nothing_to_do` when the product is empty (M or N is zero).
+lpgemm_status validate(Kind kind, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                       const void* C, const void* rs, const void* cs, bool& nothing_to_do) {
+  nothing_to_do = false;
+  if (M < 0 || N < 0 || K < 0) return LPGEMM_ERROR_INVALID_VALUE;
+  if (M > INT32_MAX || N > INT32_MAX) return LPGEMM_ERROR_INVALID_VALUE;
+  switch (kind) {
+    case KIND_I8:
+    case KIND_I8_DEQUANT:
+      if (K % 16 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+      break;
+    case KIND_I4:
+      if (K % 32 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+      break;
+    case KIND_F16:
+      if (K % 8 != 0 || K > LPGEMM_MAX_K_F16) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+      break;
+  }
+  if (M == 0 || N == 0) {
+    nothing_to_do = true;
+    return LPGEMM_SUCCESS;
+  }
+  if (!C) return LPGEMM_ERROR_INVALID_VALUE;
+  if (K > 0 && (!A || !B)) return LPGEMM_ERROR_INVALID_VALUE;
+  if (kind == KIND_I8_DEQUANT && (!rs || !cs)) return LPGEMM_ERROR_INVALID_VALUE;
+  if (!aligned16(C)) return LPGEMM_ERROR_MISALIGNED;
+  if (K > 0 && (!aligned16(A) || !aligned16(B))) return LPGEMM_ERROR_MISALIGNED;
+  if (kind == KIND_I8_DEQUANT && (!aligned4(rs) || !aligned4(cs))) return LPGEMM_ERROR_MISALIGNED;
+  return LPGEMM_SUCCESS;
+}
+
+// Tile configurations.  Large tiles give the best operand reuse; smaller ones
+// fill the 256 CUs when the product has few 256 x 256 tiles.
+enum TileCfg { TILE_256x256_W8 = 0, TILE_128x128_W4 = 1, TILE_64x64_W4 = 2 };
+
+int tiles(int64_t x, int t) { return (int)((x + t - 1) / t); }
+
+TileCfg choose_tile(int64_t M, int64_t N, int cu_count) {
+  const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
+  if (big >= cu_count) return TILE_256x256_W8;
+  const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
+  if (mid >= cu_count / 2) return TILE_128x128_W4;
+  return TILE_64x64_W4;
+}
+
+template <int KIND, int BM, int BN, int WM, int WN>
+lpgemm_status launch_cfg(GemmArgs args, hipStream_t stream) {
+  args.tiles_m = tiles(args.M, BM);
+  args.tiles_n = tiles(args.N, BN);
+  args.group_m = 8;
+  const int64_t nblocks = (int64_t)args.tiles_m * args.tiles_n;
+  if (nblocks > INT32_MAX) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  void* kargs[] = {&args};
+  const void* fn = reinterpret_cast<const void*>(&gemm_tiled<KIND, BM, BN, WM, WN>);
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(WM * WN * 64), kargs, 0, stream);
+  return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
+}
+
+template <int KIND>
+lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
+                  const float* rs, const float* cs, hipStream_t stream) {
+  bool nothing_to_do = false;
+  lpgemm_status st = validate((Kind)KIND, M, N, K, A, B, C, rs, cs, nothing_to_do);
+  if (st != LPGEMM_SUCCESS || nothing_to_do) return st;
+  DeviceInfo dev;
+  st = current_device(dev);
+  if (st != LPGEMM_SUCCESS) return st;
+
+  GemmArgs args{};
+  args.A = static_cast<const uint8_t*>(A);
+  args.B = static_cast<const uint8_t*>(B);
+  args.C = C;
+  args.row_scale = rs;
+  args.col_scale = cs;
+  args.M = (int)M;
+  args.N = (int)N;
+  int64_t row_bytes = KIND == KIND_F16 ? 2 * K : (KIND == KIND_I4 ? K / 2 : K);
+  int64_t lds_bytes = KIND == KIND_I4 ? K : row_bytes;   // int4 is expanded to int8 in LDS
+  args.row_bytes = (int)row_bytes;
+  args.k_stages = (int)((lds_bytes + kStageRowBytes - 1) / kStageRowBytes);
+
+  switch (choose_tile(M, N, dev.cu_count)) {
+    case TILE_256x256_W8: return launch_cfg<KIND, 256, 256, 2, 4>(args, stream);
+    case TILE_128x128_W4: return launch_cfg<KIND, 128, 128, 2, 2>(args, stream);
+    default: return launch_cfg<KIND, 64, 64, 2, 2>(args, stream);
+  }
+}
+
+}  // namespace
+}  // namespace lpgemm
+
+using namespace lpgemm;
+
+extern "C" {
+
+lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A, const int8_t* B,
+                        int32_t* C, hipStream_t stream) {
+  return run<KIND_I8>(M, N, K, A, B, C, nullptr, nullptr, stream);
+}
+
+lpgemm_status lpgemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t* A_packed,
+                        const uint8_t* B_packed, int32_t* C, hipStream_t stream) {
+  return run<KIND_I4>(M, N, K, A_packed, B_packed, C, nullptr, nullptr, stream);
+}
+
+lpgemm_status lpgemm_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, float* C,
+                         hipStream_t stream) {
+  return run<KIND_F16>(M, N, K, A, B, C, nullptr, nullptr, stream);
+}
+
+lpgemm_status lpgemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t* A,
+                                const int8_t* B, const float* row_scale, const float* col_scale,
+                                float* C, hipStream_t stream) {
+  return run<KIND_I8_DEQUANT>(M, N, K, A, B, C, row_scale, col_scale, stream);
+}
+
+const char* lpgemm_status_string(lpgemm_status status) {
+  switch (status) {
+    case LPGEMM_SUCCESS: return "success";
+    case LPGEMM_ERROR_INVALID_VALUE: return "invalid value (null pointer or bad size)";
+    case LPGEMM_ERROR_MISALIGNED: return "pointer not 16-byte aligned";
+    case LPGEMM_ERROR_UNSUPPORTED_SHAPE: return "unsupported K (divisibility or range)";
+    case LPGEMM_ERROR_ARCH: return "current device is not gfx950";
+    case LPGEMM_ERROR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int lpgemm_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+"""The C-ABI library without a GPU: it loads, exports what the header declares,
+and rejects bad arguments on the host before any HIP call (fake pointer
+values are safe here because validation never dereferences them)."""
+import ctypes
+
+import pytest
+
+from precision_dense_gemm_02_amd import _binding as b
+
+ENTRY = ("lpgemm_i8", "lpgemm_i4", "lpgemm_f16")
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+MISALIGNED = 0x10008
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return b.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = b.declared_functions()
+    assert set(names) == {"lpgemm_i8", "lpgemm_i4", "lpgemm_f16", "lpgemm_i8_dequant",
+                          "lpgemm_status_string", "lpgemm_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings(lib):
+    assert b.version() == 100
+    for code in range(6):
+        assert b.status_string(code)
+    assert b.status_string(99) == "unknown status"
+
+
+def _call(lib, name, M, N, K, A=FAKE, B=FAKE, C=FAKE, rs=FAKE, cs=FAKE):
+    if name == "lpgemm_i8_dequant":
+        return lib.lpgemm_i8_dequant(M, N, K, A, B, rs, cs, C, None)
+    return getattr(lib, name)(M, N, K, A, B, C, None)
+
+
+ALL = ENTRY + ("lpgemm_i8_dequant",)
+K_OK = {"lpgemm_i8": 64, "lpgemm_i4": 64, "lpgemm_f16": 64, "lpgemm_i8_dequant": 64}
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_negative_sizes(lib, name):
+    for M, N, K in ((-1, 4, 64), (4, -1, 64), (4, 4, -16)):
+        assert _call(lib, name, M, N, K) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert _call(lib, name, 2 ** 31, 4, 64) == b.LPGEMM_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("name,bad_k", [
+    ("lpgemm_i8", [8, 17, 131072, 131088]),
+    ("lpgemm_i8_dequant", [8, 24, 131072]),
+    ("lpgemm_i4", [16, 48, 131072, 131104]),
+    ("lpgemm_f16", [4, 12, 1048584]),
+])
+def test_unsupported_k(lib, name, bad_k):
+    for K in bad_k:
+        assert _call(lib, name, 4, 4, K) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE, K
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_null_pointers(lib, name):
+    assert _call(lib, name, 4, 4, 64, A=None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert _call(lib, name, 4, 4, 64, B=None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert _call(lib, name, 4, 4, 64, C=None) == b.LPGEMM_ERROR_INVALID_VALUE
+    # K = 0 is an empty sum: A and B may be NULL, C may not
+    assert _call(lib, name, 4, 4, 0, C=None) == b.LPGEMM_ERROR_INVALID_VALUE
+
+
+def test_null_scales(lib):
+    assert _call(lib, "lpgemm_i8_dequant", 4, 4, 64, rs=None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert _call(lib, "lpgemm_i8_dequant", 4, 4, 64, cs=None) == b.LPGEMM_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_misaligned(lib, name):
+    for kw in ("A", "B", "C"):
+        assert _call(lib, name, 4, 4, 64, **{kw: MISALIGNED}) == b.LPGEMM_ERROR_MISALIGNED, kw
+
+
+def test_misaligned_scales(lib):
+    assert _call(lib, "lpgemm_i8_dequant", 4, 4, 64, rs=FAKE + 2) == b.LPGEMM_ERROR_MISALIGNED
+    assert _call(lib, "lpgemm_i8_dequant", 4, 4, 64, cs=FAKE + 1) == b.LPGEMM_ERROR_MISALIGNED
+    # 4-byte alignment is enough for scales
+    # (not called with valid pointers here: that would reach the device check)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_empty_product_is_noop(lib, name):
+    # M = 0 or N = 0: success without reading any pointer (all NULL here)
+    assert _call(lib, name, 0, 5, 64, A=None, B=None, C=None, rs=None, cs=None) == 0
+    assert _call(lib, name, 5, 0, 64, A=None, B=None, C=None, rs=None, cs=None) == 0
+
+
+def test_error_order(lib):
+    # a negative size wins over a bad K and a misaligned pointer
+    assert _call(lib, "lpgemm_i8", -1, 4, 8, A=MISALIGNED) == b.LPGEMM_ERROR_INVALID_VALUE
+    # a bad K wins over a null or misaligned pointer
+    assert _call(lib, "lpgemm_i8", 4, 4, 8, A=None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    # a null pointer wins over misalignment
+    assert _call(lib, "lpgemm_i8", 4, 4, 64, A=None, B=MISALIGNED) == b.LPGEMM_ERROR_INVALID_VALUE
+
+
+def test_python_wrapper_type_checks():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros((4, 64), dtype=torch.int8)
+    with pytest.raises(TypeError):
+        b.gemm_i8(a.float(), a)
+    with pytest.raises(ValueError):                 # CPU tensors are refused
+        b.gemm_i8(a, a)
+    with pytest.raises(TypeError):
+        b.gemm_f16(a, a)
+    with pytest.raises(TypeError):
+        b.gemm_i4(a, a)
+    with pytest.raises(TypeError):
+        b.gemm_i8([1], a)
+
+
+def test_lpgemm_error_carries_status():
+    e = b.LpgemmError(b.LPGEMM_ERROR_MISALIGNED, "lpgemm_i8")
+    assert e.status == 2 and "aligned" in str(e)
+
+
+def test_signature_types(lib):
+    assert lib.lpgemm_i8.argtypes[0] is ctypes.c_int64
+    assert lib.lpgemm_i8_dequant.restype is ctypes.c_int

@@ -1,0 +1,329 @@
+"""GPU parity: the HIP kernels behind the C ABI against the CPU oracle.
+
+Integer paths and the dequantised path must match bit for bit.  FP16 must keep
+max |C - ref| / sum|a||b| <= 1e-3 against the fp64 reference over the same
+fp16 operands (the error procedure of the forum post on compiler-generated
+kernels, paragraph on hybrid FP16/FP32 accumulation); on integer-valued fp16
+operands, where fp32 accumulation is exact, it must match exactly.
+
+Shapes: the square sweeps and the LLM projection shapes of the measured
+workloads (the oracle computes all of C up to 2048, sampled rows at 4096 and
+8192, in the same launch configuration the benchmark times), ragged M/N/K that
+land on every tile configuration, K = 0, M = 0, and the int32 range limit.
+Outputs are poisoned before each call so an unwritten element cannot pass.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import precision_dense_gemm_02_amd as lp  # noqa: E402
+from precision_dense_gemm_02_amd import inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+F16_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lp.load_library()          # a GPU machine without the built library fails here, loudly
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _poison_int(M, N):
+    return torch.full((M, N), -0x5A5A5A5A, dtype=torch.int32, device="cuda")
+
+
+def _poison_f32(M, N):
+    return torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+
+
+def _sample_rows(M, n=40, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    rows.update({0, M - 1, min(M - 1, 255), min(M - 1, 256)})
+    return sorted(rows)
+
+
+def run_i8(p, rows=None):
+    M, N = p.a.shape[0], p.b_t.shape[0]
+    out = lp.gemm_i8(_dev(p.a), _dev(p.b_t), out=_poison_int(M, N))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = oracle.gemm_i8(p.a, p.b_t, rows=rows)
+    return (got if rows is None else got[rows]), ref
+
+
+def run_i4(p, K, rows=None):
+    M, N = p.a_packed.shape[0], p.b_packed.shape[0]
+    out = lp.gemm_i4(_dev(p.a_packed), _dev(p.b_packed), K, out=_poison_int(M, N))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = oracle.gemm_i4(p.a_packed, p.b_packed, K, rows=rows)
+    return (got if rows is None else got[rows]), ref
+
+
+def run_f16(p, rows=None):
+    M, N = p.a.shape[0], p.b_t.shape[0]
+    out = lp.gemm_f16(_dev(p.a), _dev(p.b_t), out=_poison_f32(M, N))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref, den = oracle.gemm_f16(p.a, p.b_t, rows=rows)
+    return (got if rows is None else got[rows]), ref, den
+
+
+def run_dq(p, rows=None):
+    M, N = p.a.shape[0], p.b_t.shape[0]
+    out = lp.gemm_i8_dequant(_dev(p.a), _dev(p.b_t), _dev(p.row_scale), _dev(p.col_scale),
+                             out=_poison_f32(M, N))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale, rows=rows)
+    return (got if rows is None else got[rows]), ref
+
+
+def assert_f16_ok(got, ref, den, tol=F16_TOL):
+    assert np.isfinite(got).all(), "unwritten or non-finite output"
+    e = oracle.f16_rel_error(got, ref, den)
+    assert e["max_rel"] <= tol, e
+    return e
+
+
+# ---------------------------------------------------------------- square sweeps
+
+@pytest.mark.parametrize("n", [512, 1024, 2048])
+def test_i8_square_full(n):
+    _say("i8 square", n)
+    got, ref = run_i8(inputs.int8_problem(n, n, n, inputs.seed_for("i8", n)))
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("n", [4096, 8192])
+def test_i8_square_sampled(n):
+    _say("i8 square sampled", n)
+    rows = _sample_rows(n, seed=n)
+    got, ref = run_i8(inputs.int8_problem(n, n, n, inputs.seed_for("i8", n)), rows)
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("n", [512, 2048])
+def test_i4_square_full(n):
+    _say("i4 square", n)
+    got, ref = run_i4(inputs.int4_problem(n, n, n, inputs.seed_for("i4", n)), n)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_i4_square_sampled_8192():
+    n = 8192
+    _say("i4 square sampled", n)
+    rows = _sample_rows(n, seed=n + 1)
+    got, ref = run_i4(inputs.int4_problem(n, n, n, inputs.seed_for("i4", n)), n, rows)
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("n", [512, 2048])
+def test_f16_square_full(n):
+    _say("f16 square", n)
+    got, ref, den = run_f16(inputs.f16_problem(n, n, n, inputs.seed_for("f16", n)))
+    assert_f16_ok(got, ref, den)
+
+
+@pytest.mark.parametrize("n", [4096, 8192])
+def test_f16_square_sampled(n):
+    _say("f16 square sampled", n)
+    rows = _sample_rows(n, seed=n + 2)
+    got, ref, den = run_f16(inputs.f16_problem(n, n, n, inputs.seed_for("f16", n)), rows)
+    assert_f16_ok(got, ref, den)
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (300, 1000, 8192), (4100, 300, 1032)])
+def test_f16_integer_valued_exact(M, N, K):
+    # every partial sum is an integer below 2^24, so fp32 accumulation is exact
+    # and a dropped or repeated k term would show as a mismatch
+    _say("f16 integer-valued", M, N, K)
+    p = inputs.f16_integer_problem(M, N, K, seed=M + N + K)
+    out = lp.gemm_f16(_dev(p.a), _dev(p.b_t), out=_poison_f32(M, N))
+    torch.cuda.synchronize()
+    ref = oracle.gemm_i8(p.a.astype(np.int8), p.b_t.astype(np.int8))
+    np.testing.assert_array_equal(out.cpu().numpy(), ref.astype(np.float32))
+
+
+# ---------------------------------------------------------------- LLM projection
+
+@pytest.mark.parametrize("M", [16, 128])
+def test_dequant_llm_full(M):
+    _say("dequant llm", M)
+    got, ref = run_dq(inputs.llm_problem(M))
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_llm_2048_sampled():
+    _say("dequant llm sampled", 2048)
+    rows = _sample_rows(2048, seed=7)
+    got, ref = run_dq(inputs.llm_problem(2048), rows)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------- ragged shapes
+
+# (M, N) pairs that select the 64x64, 128x128 and 256x256 tile configurations
+# on a 256-CU device, none of them tile multiples
+RAGGED_MN = [(1, 1), (33, 47), (257, 300), (1500, 1380), (4100, 4100)]
+
+
+@pytest.mark.parametrize("M,N", RAGGED_MN)
+@pytest.mark.parametrize("K", [16, 144, 272])
+def test_i8_ragged(M, N, K):
+    _say("i8 ragged", M, N, K)
+    got, ref = run_i8(inputs.int8_problem(M, N, K, seed=M * 7 + N * 3 + K))
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("M,N", RAGGED_MN)
+@pytest.mark.parametrize("K", [32, 160, 288])
+def test_i4_ragged(M, N, K):
+    _say("i4 ragged", M, N, K)
+    got, ref = run_i4(inputs.int4_problem(M, N, K, seed=M * 5 + N + K), K)
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("M,N", RAGGED_MN)
+@pytest.mark.parametrize("K", [8, 72, 136])
+def test_f16_ragged(M, N, K):
+    _say("f16 ragged", M, N, K)
+    got, ref, den = run_f16(inputs.f16_problem(M, N, K, seed=M + N * 11 + K))
+    assert_f16_ok(got, ref, den)
+
+
+@pytest.mark.parametrize("M,N", RAGGED_MN)
+def test_dequant_ragged(M, N):
+    _say("dequant ragged", M, N)
+    got, ref = run_dq(inputs.int8_problem(M, N, 144, seed=M + N, scales=True))
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------- degenerate cases
+
+def test_k_zero_gives_zeros():
+    _say("K = 0")
+    a = torch.empty((70, 0), dtype=torch.int8, device="cuda")
+    b = torch.empty((90, 0), dtype=torch.int8, device="cuda")
+    out = lp.gemm_i8(a, b, out=_poison_int(70, 90))
+    torch.cuda.synchronize()
+    assert (out == 0).all()
+    outf = lp.gemm_f16(a.half(), b.half(), out=_poison_f32(70, 90))
+    torch.cuda.synchronize()
+    assert (outf == 0).all()
+    a4 = torch.empty((70, 0), dtype=torch.uint8, device="cuda")
+    b4 = torch.empty((90, 0), dtype=torch.uint8, device="cuda")
+    out4 = lp.gemm_i4(a4, b4, 0, out=_poison_int(70, 90))
+    torch.cuda.synchronize()
+    assert (out4 == 0).all()
+
+
+def test_empty_m_and_n():
+    _say("M = 0, N = 0")
+    a = torch.zeros((0, 64), dtype=torch.int8, device="cuda")
+    b = torch.zeros((5, 64), dtype=torch.int8, device="cuda")
+    assert lp.gemm_i8(a, b).shape == (0, 5)
+    assert lp.gemm_i8(b, a).shape == (5, 0)
+
+
+def test_int32_range_limit():
+    # largest K that keeps every exact int8 sum in int32, all products 2^14
+    M, N, K = 64, 80, 131056
+    _say("int32 range", M, N, K)
+    a = np.full((M, K), -128, np.int8)
+    b = np.full((N, K), -128, np.int8)
+    b[1::2] = 127
+    got, ref = run_i8(inputs.Int8Problem(a, b))
+    np.testing.assert_array_equal(got, ref)
+    assert ref.max() == 16384 * K and ref.min() == -16256 * K
+
+
+def test_int4_range_limit():
+    M, N, K = 64, 48, 131040
+    _say("int4 range", M, N, K)
+    a = np.full((M, K), -8, np.int8)
+    b = np.full((N, K), -8, np.int8)
+    b[1::2] = 7
+    p = inputs.Int4Problem(a, b, inputs.pack_int4(a), inputs.pack_int4(b))
+    got, ref = run_i4(p, K)
+    np.testing.assert_array_equal(got, ref)
+    assert ref.max() == 64 * K and ref.min() == -56 * K
+
+
+# ---------------------------------------------------------------- consistency
+
+def test_cross_path_int4_int8_f16():
+    # the same small integers through the three paths give one answer
+    M, N, K = 700, 530, 1024
+    _say("cross path", M, N, K)
+    p = inputs.int4_problem(M, N, K, seed=99)
+    c4 = lp.gemm_i4(_dev(p.a_packed), _dev(p.b_packed), K)
+    c8 = lp.gemm_i8(_dev(p.a_values), _dev(p.b_values))
+    cf = lp.gemm_f16(_dev(p.a_values.astype(np.float16)), _dev(p.b_values.astype(np.float16)))
+    torch.cuda.synchronize()
+    assert torch.equal(c4, c8)
+    assert torch.equal(cf, c8.float())
+
+
+@pytest.mark.parametrize("kind", ["i8", "f16", "i4"])
+def test_repeat_is_bitwise_identical(kind):
+    n = 2048
+    _say("repeat", kind, n)
+    if kind == "i8":
+        p = inputs.int8_problem(n, n, n, 5)
+        a, b = _dev(p.a), _dev(p.b_t)
+        f = lambda: lp.gemm_i8(a, b)  # noqa: E731
+    elif kind == "i4":
+        p = inputs.int4_problem(n, n, n, 5)
+        a, b = _dev(p.a_packed), _dev(p.b_packed)
+        f = lambda: lp.gemm_i4(a, b, n)  # noqa: E731
+    else:
+        p = inputs.f16_problem(n, n, n, 5)
+        a, b = _dev(p.a), _dev(p.b_t)
+        f = lambda: lp.gemm_f16(a, b)  # noqa: E731
+    first = f()
+    for _ in range(5):
+        again = f()
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int32), again.view(torch.int32))
+
+
+def test_side_stream():
+    n = 1024
+    _say("side stream", n)
+    p = inputs.int8_problem(n, n, n, 6)
+    a, b = _dev(p.a), _dev(p.b_t)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = lp.gemm_i8(a, b, out=_poison_int(n, n))
+    s.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), oracle.gemm_i8(p.a, p.b_t))
+
+
+def test_back_to_back_launches():
+    # many launches in a row on one stream, outputs checked at the end
+    n = 1024
+    _say("back to back", n)
+    probs = [inputs.int8_problem(n, n, n, 40 + i) for i in range(4)]
+    devs = [(_dev(p.a), _dev(p.b_t)) for p in probs]
+    outs = [lp.gemm_i8(a, b, out=_poison_int(n, n)) for a, b in devs for _ in range(3)]
+    torch.cuda.synchronize()
+    for i, p in enumerate(probs):
+        ref = oracle.gemm_i8(p.a, p.b_t)
+        for r in range(3):
+            np.testing.assert_array_equal(outs[3 * i + r].cpu().numpy(), ref)

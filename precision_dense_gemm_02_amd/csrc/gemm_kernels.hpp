@@ -24,8 +24,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lpgemm {
 
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -309,6 +312,568 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tiled(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * frag_half + (e & 3);
+        if (col_ok && row < p.M) {
+          const size_t idx = (size_t)row * p.N + col;
+          if constexpr (KIND == KIND_F16) {
+            ((float*)p.C)[idx] = acc[i][j][e];
+          } else if constexpr (KIND == KIND_I4) {
+            ((int32_t*)p.C)[idx] = acc[i][j][e] >> 8;   // undo the 16 x 16 scaling
+          } else if constexpr (KIND == KIND_I8_DEQUANT) {
+            float t = (float)acc[i][j][e];
+            t = t * p.row_scale[row];
+            t = t * cs;
+            ((float*)p.C)[idx] = t;
+          } else {
+            ((int32_t*)p.C)[idx] = acc[i][j][e];
+          }
+        }
+      }
+    }
+  }
+}
+
+
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS loads, counter waits and barriers written out explicitly.
+//
+// The compiler's __syncthreads() carries a workgroup fence that waits for
+// every outstanding vector-memory load (vmcnt(0)), which would drain the
+// whole multi-stage load pipeline at each barrier.  The pipelined kernels
+// therefore issue their direct-to-LDS loads, their vmcnt(N) waits and their
+// barriers themselves: the "memory" clobbers keep the compiler from moving
+// LDS accesses across them, and the counts are derived in each kernel.
+
+// Raw buffer resource (gfx9 V#) over [base, base + bytes); offsets at or past
+// `bytes` read as zero.  All fields are made wave-uniform.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu));   // stride 0
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = kBufferWord3;
+  return r;
+}
+
+// Each lane loads 16 bytes at buffer offset `voff`; lane l's bytes land at
+// LDS byte address lds_addr + 16 l.  M0 carries the LDS address for the
+// load and is restored afterwards; one wait state separates the M0 write
+// from its use.
+__device__ __forceinline__ void lds_dma_16(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)p);
+}
+
+// ---------------------------------------------------------------------------
+// Four-wave kernel with direct-to-LDS loads and an LDS-staged epilogue.
+//
+// A workgroup of 4 waves (one per SIMD) computes a BM x BN tile; each wave
+// owns a (BM/2) x (BN/2) quadrant made of 32 x 32 MFMA blocks, so that at
+// BM = BN = 256 every wave keeps 16 independent accumulator chains in flight
+// (a 32 x 32 MFMA needs about 8 per SIMD to run at full rate) and reads half
+// as many LDS bytes per MAC as an 8-wave 128 x 64 split.
+//
+// Operand rows stay K-contiguous in LDS, ROWB (64 or 128) bytes per row per
+// K-stage: int8 or fp16 values, or packed int4 (int4 stays packed in LDS and
+// is expanded to int8 in registers after the fragment read).  Global data
+// goes straight into LDS with 16-byte buffer loads (lane l writes 16 bytes at
+// base + 16 l), so the swizzle is applied by choosing which global chunk each
+// lane fetches.  STAGES buffers form a ring: the loads of stage s+STAGES-1 are
+// issued during stage s, so STAGES-1 stages of latency are hidden; the
+// barrier that publishes stage s+1 sits in the middle of stage s's last
+// K-step, and the first fragments of stage s+1 are read while the remaining
+// MFMAs of stage s execute.
+//
+// Epilogue: each wave transposes its accumulators through LDS (64 rows at a
+// time) so that every lane stores 16 contiguous bytes and a store
+// instruction covers two 512-byte row segments.
+template <int ROWB>
+struct RowLayout;
+
+// 128-byte rows: 8 chunks; the chunk position XORs a 3-bit function of the
+// row, conflict-free for fragment reads that take one chunk from each of 16
+// consecutive rows (64 banks) or 8 consecutive rows (32 banks).
+template <>
+struct RowLayout<128> {
+  static constexpr int kChunks = 8;
+  __device__ static int off(int r, int c) { return r * 128 + (swizzle_chunk(r, c) << 4); }
+  __device__ static int pos(int r, int c) { return swizzle_chunk(r, c); }
+};
+
+// 64-byte rows: 4 chunks; pairs of rows share a 128-byte line.  The chunk
+// position XORs a 2-bit function of the line chosen so that rows m, m+4,
+// m+8, m+12 (which share banks at 64 banks) and rows of one parity among 8
+// consecutive rows (at 32 banks) all land on distinct chunk positions.
+template <>
+struct RowLayout<64> {
+  static constexpr int kChunks = 4;
+  __device__ static int f(int r) {
+    const int L = r >> 1;
+    return ((((L >> 1) ^ (L >> 2)) & 1) << 1) | ((L ^ (L >> 1)) & 1);
+  }
+  __device__ static int off(int r, int c) { return r * 64 + ((c ^ f(r)) << 4); }
+  __device__ static int pos(int r, int c) { return c ^ f(r); }
+};
+
+template <int KIND, int BM, int BN, int STAGES, int ROWB>
+__global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
+  using Acc = typename KindTraits<KIND>::Acc;
+  using Layout = RowLayout<ROWB>;
+  constexpr bool I4 = KIND == KIND_I4;
+  constexpr int kStepBytes = I4 ? 16 : 32;           // row bytes one MFMA K-step consumes
+  constexpr int KSTEPS = ROWB / kStepBytes;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM % 2 == 0 && TN >= 1 && BM % 128 == 0 && BN % 64 == 0, "tile");
+  constexpr int kRows = BM + BN;
+  constexpr int kStage = kRows * ROWB;
+  constexpr int kRowsPerLoad = 1024 / ROWB;          // rows one 1 KiB wave load fills
+  constexpr int kLoads = kRows / kRowsPerLoad;       // 1 KiB loads per stage
+  static_assert(kLoads % 4 == 0 && (BM / kRowsPerLoad) % 4 == 0, "loads per wave");
+  constexpr int kSlots = kLoads / 4;                 // per wave per stage
+  constexpr int kSlotsA = BM / kRowsPerLoad / 4;
+  static_assert((STAGES - 2) * kSlots <= 63, "vmcnt range");
+  constexpr int kMainLds = STAGES * kStage;
+  // epilogue staging: per wave 64 rows of WTN 4-byte values plus 32 B padding
+  constexpr int kEpiPitch = WTN * 4 + 32;
+  constexpr int kEpiRows = 64;
+  constexpr int kEpiLds = 4 * kEpiRows * kEpiPitch;
+  constexpr int kLds = kMainLds > kEpiLds ? kMainLds : kEpiLds;
+  static_assert(kLds <= 160 * 1024, "LDS");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int rows_a = min(BM, p.M - m0);
+  const int rows_b = min(BN, p.N - n0);
+  const i32x4 rsrc_a = make_rsrc(p.A + (size_t)m0 * p.row_bytes, rows_a * p.row_bytes);
+  const i32x4 rsrc_b = make_rsrc(p.B + (size_t)n0 * p.row_bytes, rows_b * p.row_bytes);
+  const uint32_t smem_lds = lds_address(smem);
+
+  // Load slot t of this wave fills stage rows kRowsPerLoad*g .. (g = 4t +
+  // wave): lane l writes row kRowsPerLoad*g + l / kChunks at chunk position
+  // l % kChunks, so it fetches the global chunk whose swizzled position that is.
+  uint32_t slot_off[kSlots];
+  uint32_t slot_col[kSlots];
+#pragma unroll
+  for (int t = 0; t < kSlots; ++t) {
+    const int g = 4 * t + wave;
+    const int lrow = kRowsPerLoad * g + lane / Layout::kChunks;
+    const int c = Layout::pos(lrow, lane % Layout::kChunks);   // XOR swizzle is an involution
+    const int grow = t < kSlotsA ? lrow : lrow - BM;
+    slot_off[t] = grow * p.row_bytes + c * 16;
+    slot_col[t] = c * 16;
+  }
+
+  auto issue_load = [&](int t, int s) {
+    const uint32_t kbyte = (uint32_t)s * ROWB;
+    const int g = 4 * t + wave;
+    const bool in_row = kbyte + slot_col[t] < (uint32_t)p.row_bytes;
+    const uint32_t off = in_row ? slot_off[t] + kbyte : kOutOfRange;
+    lds_dma_16(t < kSlotsA ? rsrc_a : rsrc_b, smem_lds + (s % STAGES) * kStage + g * 1024, off);
+  };
+
+  // Fragment addressing: lane l reads row (l & 31) of a 32-row block; blocks
+  // start at multiples of 32 rows, which leaves the swizzle unchanged.
+  const int fr = lane & 31, fh = lane >> 5;
+  const int a_row_base = (wm * WTM) * ROWB;
+  const int b_row_base = (BM + wn * WTN) * ROWB;
+  auto frag_off = [&](int kk) -> int {
+    if constexpr (I4) return Layout::off(fr, kk) + fh * 8;       // 8 packed bytes
+    else return Layout::off(fr, 2 * kk + fh);                     // 16 bytes
+  };
+
+  using Raw = typename std::conditional<I4, i32x2_t, i32x4>::type;
+  Raw fa[2][TM], fb[2][TN];
+
+  auto read_frags = [&](int s, int kk, int dst) {
+    const uint8_t* base = smem + (s % STAGES) * kStage;
+    const int off = frag_off(kk);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[dst][i] = *(const Raw*)(base + a_row_base + i * 32 * ROWB + off);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      fb[dst][j] = *(const Raw*)(base + b_row_base + j * 32 * ROWB + off);
+  };
+
+  auto operand = [&](const Raw& r) -> i32x4 {
+    if constexpr (I4) {
+      uint32_t lo0, hi0, lo1, hi1;
+      expand_int4((uint32_t)r.x, lo0, hi0);
+      expand_int4((uint32_t)r.y, lo1, hi1);
+      return i32x4{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
+    } else {
+      return r;
+    }
+  };
+
+  Acc acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  auto compute = [&](int src, int first, int last) {
+    i32x4 a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = operand(fa[src][i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = operand(fb[src][j]);
+#pragma unroll
+    for (int x = 0; x < TM * TN; ++x) {
+      if (x < first || x >= last) continue;
+      const int i = x / TN, j = x % TN;
+      acc[i][j] = mfma<KIND>(a[i], b[j], acc[i][j]);
+    }
+  };
+
+  constexpr int kMfma = TM * TN;
+  constexpr int kReads = TM + TN;
+  // loads of one stage are spread over K-steps 0 .. KSTEPS-2 (or step 0)
+  constexpr int kLoadSteps = KSTEPS > 1 ? KSTEPS - 1 : 1;
+  constexpr int kLoadsPerStep = (kSlots + kLoadSteps - 1) / kLoadSteps;
+  auto interleave = [&](int mfmas, int reads, int loads) {
+#pragma unroll
+    for (int x = 0; x < kMfma; ++x) {
+      if (x >= mfmas) break;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+      if (x < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      if (x < loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+    }
+  };
+
+  const int nks = p.k_stages;   // 0 when K = 0: C is written as zeros
+  if (nks > 0) {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+#pragma unroll
+      for (int t = 0; t < kSlots; ++t) issue_load(t, s);
+    wait_vmcnt<(STAGES - 2) * kSlots>();   // own loads of stage 0
+    block_barrier();                       // everyone's
+    read_frags(0, 0, 0);
+  }
+  for (int s = 0; s < nks; ++s) {
+    // loads for stage s + STAGES - 1 (past the last stage they only write
+    // zeros that nobody reads)
+    const int sl = s + STAGES - 1;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int src = kk & 1, dst = src ^ 1;
+      int nl = 0;
+      if (kk < kLoadSteps) {
+#pragma unroll
+        for (int t = 0; t < kSlots; ++t) {
+          if (t / kLoadsPerStep != kk) continue;
+          issue_load(t, sl);
+          ++nl;
+        }
+      }
+      if (kk + 1 < KSTEPS) {
+        read_frags(s, kk + 1, dst);
+        compute(src, 0, kMfma);
+        interleave(kMfma, kReads, nl);
+      } else {
+        compute(src, 0, kMfma / 2);
+        interleave(kMfma / 2, 0, nl);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(STAGES - 2) * kSlots>();   // own loads of stage s+1 landed
+        wait_lgkmcnt0();                       // own reads of stage s done
+        block_barrier();                       // ... everyone's
+        read_frags(s + 1, 0, dst);
+        compute(src, kMfma / 2, kMfma);
+        interleave(kMfma / 2, kReads, 0);
+      }
+    }
+  }
+
+  // ------------------------------------------------------------------ epilogue
+  // Element e of lane l in a 32x32 block is row 8*(e/4) + 4*(l/32) + e%4,
+  // column l%32 of the block.
+  auto value = [&](int i, int j, int e, int row, int col) -> uint32_t {
+    if constexpr (KIND == KIND_F16) {
+      return __builtin_bit_cast(uint32_t, (float)acc[i][j][e]);
+    } else if constexpr (KIND == KIND_I4) {
+      return (uint32_t)(acc[i][j][e] >> 8);   // undo the 16 x 16 scaling
+    } else if constexpr (KIND == KIND_I8_DEQUANT) {
+      float t = (float)acc[i][j][e];
+      t = t * p.row_scale[row];
+      t = t * p.col_scale[col];
+      return __builtin_bit_cast(uint32_t, t);
+    } else {
+      return (uint32_t)acc[i][j][e];
+    }
+  };
+
+  // Outstanding loads (all past the last stage) must land before LDS is
+  // reused; the barrier then also covers every wave's fragment reads.
+  wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  const bool interior = m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 3) == 0;
+  if (interior) {
+    block_barrier();   // every wave is done with the operand stages
+    uint8_t* stage_out = smem + wave * kEpiRows * kEpiPitch;
+    const int row0 = m0 + wm * WTM;
+    const int col0 = n0 + wn * WTN;
+#pragma unroll
+    for (int half = 0; half < TM / 2; ++half) {
+      // accumulator blocks i = 2*half, 2*half+1 cover 64 rows of the quadrant
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * half + ii;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = ii * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+            const int c = j * 32 + fr;
+            *(uint32_t*)(stage_out + r * kEpiPitch + c * 4) =
+                value(i, j, e, row0 + half * 64 + r, col0 + c);
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes done
+      // each lane stores 16 bytes; lanes 0..WTN/4-1 cover one row
+      constexpr int kLanesPerRow = WTN / 4;
+      constexpr int kRowsPerStore = 64 / kLanesPerRow;
+#pragma unroll
+      for (int r0 = 0; r0 < kEpiRows; r0 += kRowsPerStore) {
+        const int r = r0 + lane / kLanesPerRow;
+        const int c = (lane % kLanesPerRow) * 4;
+        const i32x4 v = *(const i32x4*)(stage_out + r * kEpiPitch + c * 4);
+        const size_t idx = (size_t)(row0 + half * 64 + r) * p.N + col0 + c;
+        *(i32x4*)((uint32_t*)p.C + idx) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next half overwrites
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * WTN + j * 32 + fr;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+          if (col < p.N && row < p.M) ((uint32_t*)p.C)[(size_t)row * p.N + col] = value(i, j, e, row, col);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Eight-wave ping-pong kernel.
+//
+// A 256 x 256 tile is split into eight 128 x 64 wave tiles; waves w and w+4
+// share SIMD w % 4.  The two groups of four waves alternate between a memory
+// phase (read this stage's operand fragments from LDS into registers, issue
+// the direct-to-LDS loads of a later stage) and a compute phase (only MFMAs,
+// on operands already in registers), separated by workgroup barriers and
+// offset by one barrier, so that on every SIMD one wave keeps the matrix
+// core busy while the other one waits on memory.  A single wave that mixes
+// both kinds of instructions stalls its own MFMA issue whenever a memory
+// instruction or a wait on one blocks.
+//
+// Barrier schedule (group A = waves 0-3, group B = waves 4-7; b_n = n-th
+// barrier after the prologue):
+//   A: MEM(0) b1 COMP(0) b2 MEM(1) b3 COMP(1) b4 ...   MEM(s) in (b_2s, b_2s+1)
+//   B: b1 MEM(0) b2 COMP(0) b3 MEM(1) b4 ...           MEM(s) in (b_2s+1, b_2s+2)
+// In MEM(s) a wave reads stage s, issues its loads for stage s+3 into buffer
+// (s+3) % 4 = (s-1) % 4, and waits for its own loads of stage s+1.  Hence
+// every load of stage s has landed before b_2s (A's wait in MEM(s-1) precedes
+// b_2s-1, B's precedes b_2s), and every read of stage s-1 has finished
+// before b_2s, after which both groups first overwrite buffer (s-1) % 4.
+template <int KIND, int ROWB>
+__global__ __launch_bounds__(512) void gemm_pingpong(GemmArgs p) {
+  using Acc = typename KindTraits<KIND>::Acc;
+  using Layout = RowLayout<ROWB>;
+  constexpr bool I4 = KIND == KIND_I4;
+  constexpr int BM = 256, BN = 256, STAGES = 4;
+  constexpr int kStepBytes = I4 ? 16 : 32;
+  constexpr int KSTEPS = ROWB / kStepBytes;
+  constexpr int WTM = 128, WTN = 64;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int kRows = BM + BN;
+  constexpr int kStage = kRows * ROWB;
+  constexpr int kRowsPerLoad = 1024 / ROWB;
+  constexpr int kLoads = kRows / kRowsPerLoad;      // 1 KiB loads per stage
+  constexpr int kSlots = kLoads / 8;                // per wave per stage
+  constexpr int kLoadsA = BM / kRowsPerLoad;
+  static_assert(kLoads % 8 == 0 && kLoadsA % 8 == 0, "loads per wave");
+  static_assert(2 * kSlots <= 63, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;          // 0: A, 1: B
+  const int wm = group, wn = wave & 3;  // group A owns rows 0..127 of the tile
+
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int rows_a = min(BM, p.M - m0);
+  const int rows_b = min(BN, p.N - n0);
+  const i32x4 rsrc_a = make_rsrc(p.A + (size_t)m0 * p.row_bytes, rows_a * p.row_bytes);
+  const i32x4 rsrc_b = make_rsrc(p.B + (size_t)n0 * p.row_bytes, rows_b * p.row_bytes);
+  const uint32_t smem_lds = lds_address(smem);
+
+  // slot t of this wave: the (8t + wave)-th 1 KiB piece of the stage
+  uint32_t slot_off[kSlots];
+  uint32_t slot_col[kSlots];
+#pragma unroll
+  for (int t = 0; t < kSlots; ++t) {
+    const int g = 8 * t + wave;
+    const int lrow = kRowsPerLoad * g + lane / Layout::kChunks;
+    const int c = Layout::pos(lrow, lane % Layout::kChunks);
+    const int grow = g < kLoadsA ? lrow : lrow - BM;
+    slot_off[t] = grow * p.row_bytes + c * 16;
+    slot_col[t] = c * 16;
+  }
+  auto issue_load = [&](int t, int s) {
+    const uint32_t kbyte = (uint32_t)s * ROWB;
+    const int g = 8 * t + wave;
+    const bool in_row = kbyte + slot_col[t] < (uint32_t)p.row_bytes;
+    const uint32_t off = in_row ? slot_off[t] + kbyte : kOutOfRange;
+    lds_dma_16(g < kLoadsA ? rsrc_a : rsrc_b, smem_lds + (s % STAGES) * kStage + g * 1024, off);
+  };
+
+  const int fr = lane & 31, fh = lane >> 5;
+  const int a_row_base = (wm * WTM) * ROWB;
+  const int b_row_base = (BM + wn * WTN) * ROWB;
+  auto frag_off = [&](int kk) -> int {
+    if constexpr (I4) return Layout::off(fr, kk) + fh * 8;
+    else return Layout::off(fr, 2 * kk + fh);
+  };
+
+  using Raw = typename std::conditional<I4, i32x2_t, i32x4>::type;
+  Raw fa[KSTEPS][TM], fb[KSTEPS][TN];
+
+  auto read_stage = [&](int s) {
+    const uint8_t* base = smem + (s % STAGES) * kStage;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int off = frag_off(kk);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[kk][i] = *(const Raw*)(base + a_row_base + i * 32 * ROWB + off);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[kk][j] = *(const Raw*)(base + b_row_base + j * 32 * ROWB + off);
+    }
+  };
+
+  auto operand = [&](const Raw& r) -> i32x4 {
+    if constexpr (I4) {
+      uint32_t lo0, hi0, lo1, hi1;
+      expand_int4((uint32_t)r.x, lo0, hi0);
+      expand_int4((uint32_t)r.y, lo1, hi1);
+      return i32x4{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
+    } else {
+      return r;
+    }
+  };
+
+  Acc acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  auto compute_stage = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      i32x4 a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = operand(fa[kk][i]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = operand(fb[kk][j]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma<KIND>(a[i], b[j], acc[i][j]);
+    }
+  };
+
+  const int nks = p.k_stages;   // 0 when K = 0: C is written as zeros
+  if (nks > 0) {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+#pragma unroll
+      for (int t = 0; t < kSlots; ++t) issue_load(t, s);
+    wait_vmcnt<2 * kSlots>();            // own loads of stage 0
+    block_barrier();                     // everyone's
+    if (group == 1) block_barrier();     // B runs one barrier behind
+    for (int s = 0; s < nks; ++s) {
+      // memory phase
+      read_stage(s);
+#pragma unroll
+      for (int t = 0; t < kSlots; ++t) issue_load(t, s + STAGES - 1);
+      wait_vmcnt<2 * kSlots>();          // own loads of stage s+1
+      wait_lgkmcnt0();                   // own fragment reads of stage s
+      block_barrier();
+      // compute phase
+      __builtin_amdgcn_s_setprio(1);
+      compute_stage();
+      __builtin_amdgcn_s_setprio(0);
+      block_barrier();
+    }
+    if (group == 0) block_barrier();     // same barrier count for both groups
+  }
+  wait_vmcnt<0>();                       // loads past the last stage
+
+  // Epilogue: element e of lane l in a 32x32 block is row 8*(e/4) + 4*(l/32)
+  // + e%4, column l%32.
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + fr;
+      const bool col_ok = col < p.N;
+      float cs = 0.f;
+      if constexpr (KIND == KIND_I8_DEQUANT) cs = col_ok ? p.col_scale[col] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
         if (col_ok && row < p.M) {
           const size_t idx = (size_t)row * p.N + col;
           if constexpr (KIND == KIND_F16) {

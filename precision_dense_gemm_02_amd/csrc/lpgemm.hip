@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -80,30 +81,61 @@ lpgemm_status validate(Kind kind, int64_t M, int64_t N, int64_t K, const void* A
   return LPGEMM_SUCCESS;
 }
 
-// Tile configurations.  Large tiles give the best operand reuse; smaller ones
-// fill the 256 CUs when the product has few 256 x 256 tiles.
-enum TileCfg { TILE_256x256_W8 = 0, TILE_128x128_W4 = 1, TILE_64x64_W4 = 2 };
+// Kernel configurations.  The four-wave direct-to-LDS kernel with 256 x 256
+// tiles has the best operand reuse; smaller tiles fill the 256 CUs when the
+// product has few 256 x 256 tiles.
+enum KernelCfg {
+  CFG_256_S2_R128 = 0,   // 4 waves, 256 x 256, 2 stages of 128-byte rows
+  CFG_256_S4_R64 = 1,    // 4 waves, 256 x 256, 4 stages of 64-byte rows
+  CFG_256_S3_R64 = 2,    // 4 waves, 256 x 256, 3 stages of 64-byte rows
+  CFG_128_S4_R64 = 3,    // 4 waves, 128 x 128, 4 stages of 64-byte rows
+  CFG_V1_256x256 = 4,    // 8 waves, 128 x 64 per wave, register-staged loads
+  CFG_V1_128x128 = 5,    // 4 waves, 64 x 64 per wave, register-staged loads
+  CFG_V1_64x64 = 6,      // 4 waves, 32 x 32 per wave, register-staged loads
+  CFG_PP_R64 = 7,        // 8 waves ping-pong, 256 x 256, 4 stages of 64-byte rows
+  CFG_COUNT = 8
+};
+
+// Row bytes of one LDS K-stage for a configuration (the register-staged
+// kernels expand int4 to int8 on the way into LDS, 128 values per stage).
+int stage_row_bytes(KernelCfg c) {
+  return (c == CFG_256_S4_R64 || c == CFG_256_S3_R64 || c == CFG_128_S4_R64 || c == CFG_PP_R64) ? 64
+                                                                                                 : 128;
+}
+bool expands_int4_in_lds(KernelCfg c) { return c >= CFG_V1_256x256 && c <= CFG_V1_64x64; }
 
 int tiles(int64_t x, int t) { return (int)((x + t - 1) / t); }
 
-TileCfg choose_tile(int64_t M, int64_t N, int cu_count) {
-  const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
-  if (big >= cu_count) return TILE_256x256_W8;
-  const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
-  if (mid >= cu_count / 2) return TILE_128x128_W4;
-  return TILE_64x64_W4;
+// LPGEMM_FORCE_CONFIG=<n> pins the kernel configuration (one knob at a time
+// for ablations); unset or out of range means automatic selection.  Read on
+// every call so that a test can walk through the configurations.
+int forced_config() {
+  const char* e = std::getenv("LPGEMM_FORCE_CONFIG");
+  if (!e || !*e) return -1;
+  char* end = nullptr;
+  const long v = std::strtol(e, &end, 10);
+  return (end && *end == 0 && v >= 0 && v < CFG_COUNT) ? (int)v : -1;
 }
 
-template <int KIND, int BM, int BN, int WM, int WN>
-lpgemm_status launch_cfg(GemmArgs args, hipStream_t stream) {
+KernelCfg choose_config(int64_t M, int64_t N, int cu_count) {
+  const int f = forced_config();
+  if (f >= 0) return (KernelCfg)f;
+  const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
+  if (big >= cu_count) return CFG_256_S2_R128;
+  const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
+  if (mid >= cu_count / 2) return CFG_128_S4_R64;
+  return CFG_V1_64x64;
+}
+
+template <int BM, int BN>
+lpgemm_status launch(const void* fn, GemmArgs args, int threads, hipStream_t stream) {
   args.tiles_m = tiles(args.M, BM);
   args.tiles_n = tiles(args.N, BN);
   args.group_m = 8;
   const int64_t nblocks = (int64_t)args.tiles_m * args.tiles_n;
   if (nblocks > INT32_MAX) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
   void* kargs[] = {&args};
-  const void* fn = reinterpret_cast<const void*>(&gemm_tiled<KIND, BM, BN, WM, WN>);
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(WM * WN * 64), kargs, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(threads), kargs, 0, stream);
   return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
 }
 
@@ -125,15 +157,31 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   args.col_scale = cs;
   args.M = (int)M;
   args.N = (int)N;
-  int64_t row_bytes = KIND == KIND_F16 ? 2 * K : (KIND == KIND_I4 ? K / 2 : K);
-  int64_t lds_bytes = KIND == KIND_I4 ? K : row_bytes;   // int4 is expanded to int8 in LDS
+  const int64_t row_bytes = KIND == KIND_F16 ? 2 * K : (KIND == KIND_I4 ? K / 2 : K);
   args.row_bytes = (int)row_bytes;
-  args.k_stages = (int)((lds_bytes + kStageRowBytes - 1) / kStageRowBytes);
 
-  switch (choose_tile(M, N, dev.cu_count)) {
-    case TILE_256x256_W8: return launch_cfg<KIND, 256, 256, 2, 4>(args, stream);
-    case TILE_128x128_W4: return launch_cfg<KIND, 128, 128, 2, 2>(args, stream);
-    default: return launch_cfg<KIND, 64, 64, 2, 2>(args, stream);
+  const KernelCfg cfg = choose_config(M, N, dev.cu_count);
+  const int64_t stage_bytes = (KIND == KIND_I4 && expands_int4_in_lds(cfg)) ? K : row_bytes;
+  const int rowb = stage_row_bytes(cfg);
+  args.k_stages = (int)((stage_bytes + rowb - 1) / rowb);
+
+  switch (cfg) {
+    case CFG_256_S2_R128:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
+    case CFG_256_S4_R64:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 4, 64>, args, 256, stream);
+    case CFG_256_S3_R64:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 3, 64>, args, 256, stream);
+    case CFG_128_S4_R64:
+      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 64>, args, 256, stream);
+    case CFG_V1_256x256:
+      return launch<256, 256>((const void*)&gemm_tiled<KIND, 256, 256, 2, 4>, args, 512, stream);
+    case CFG_V1_128x128:
+      return launch<128, 128>((const void*)&gemm_tiled<KIND, 128, 128, 2, 2>, args, 256, stream);
+    case CFG_PP_R64:
+      return launch<256, 256>((const void*)&gemm_pingpong<KIND, 64>, args, 512, stream);
+    default:
+      return launch<64, 64>((const void*)&gemm_tiled<KIND, 64, 64, 2, 2>, args, 256, stream);
   }
 }
 

@@ -262,6 +262,9 @@ def main():
                     help="comma-separated extra workloads timed in the same run ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (--steps times); its "
+                         "FETCH_SIZE/WRITE_SIZE counters calibrate the traffic figures")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -273,6 +276,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20 // 4
+        src = torch.arange(n, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": args.steps}), flush=True)
+        return
+
     import precision_dense_gemm_02_amd as lp
     lp.load_library()
 

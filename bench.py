@@ -151,6 +151,32 @@ class Workload:
         return f"bit-exact over {len(rows)} sampled rows" if ok else "FAIL"
 
 
+def time_graph(w: Workload, steps: int, warmup: int) -> dict:
+    """Capture `steps` launches in one HIP graph and time its replay: GPU time
+    only, without the host's per-call overhead (which dominates below about
+    20 us per GEMM)."""
+    import torch
+    for i in range(max(warmup, 3)):
+        w.launch(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            w.launch(i)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": ms, "kernel_ms_avg": ms, "kernel_ms_min": ms, "kernel_ms_median": ms}
+
+
 def time_workload(w: Workload, steps: int, warmup: int) -> dict:
     import torch
     stream = torch.cuda.current_stream()
@@ -235,12 +261,13 @@ def cpu_baseline(w: Workload, seconds: float) -> dict:
                       f"({nrows * w.N} outputs)"}
 
 
-def measure(name: str, steps: int, warmup: int) -> tuple:
+def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
     w = Workload(name)
-    t = time_workload(w, steps, warmup)
+    t = time_graph(w, steps, warmup) if graph else time_workload(w, steps, warmup)
     r = roofline(w, t)
     value = w.ops / (t["ms_per_step"] / 1e3) / 1e12
     rec = {"workload": name, "value": round(value, 1), "unit": UNIT[w.kind],
+           "timing": "hip graph replay" if graph else "eager launches",
            "ms_per_step": round(t["ms_per_step"], 5),
            "kernel_ms_avg": round(t["kernel_ms_avg"], 5),
            "kernel_ms_min": round(t["kernel_ms_min"], 5),
@@ -261,6 +288,9 @@ def main():
     ap.add_argument("--also", default="i4-8192,f16-8192",
                     help="comma-separated extra workloads timed in the same run ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as one captured HIP graph (GPU time without host "
+                         "launch overhead; for the small shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (--steps times); its "
@@ -289,12 +319,12 @@ def main():
     import precision_dense_gemm_02_amd as lp
     lp.load_library()
 
-    w, head = measure(args.workload, args.steps, args.warmup)
+    w, head = measure(args.workload, args.steps, args.warmup, args.graph)
     print(f"# {head['workload']}: {head['value']} {head['unit']} ({head['parity']})",
           file=sys.stderr, flush=True)
     also = []
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
-        _, rec = measure(name, args.steps, args.warmup)
+        _, rec = measure(name, args.steps, args.warmup, args.graph)
         print(f"# {rec['workload']}: {rec['value']} {rec['unit']} ({rec['parity']})",
               file=sys.stderr, flush=True)
         also.append(rec)

@@ -42,5 +42,30 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBES = os.path.join(ROOT, "probes")
+
+
+def build_probes(verbose: bool = False) -> list:
+    """Compile the stand-alone measurement probes in probes/ (executables
+    next to their sources; not part of the library)."""
+    built = []
+    for name in sorted(os.listdir(PROBES)) if os.path.isdir(PROBES) else []:
+        if not name.endswith(".hip"):
+            continue
+        src = os.path.join(PROBES, name)
+        exe = src[:-4]
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", exe]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {name}:\n{r.stderr}")
+        built.append(exe)
+    return built
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    for exe in build_probes(verbose=True):
+        print(exe)

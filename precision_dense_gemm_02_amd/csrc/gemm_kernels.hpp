@@ -894,4 +894,156 @@ __global__ __launch_bounds__(512) void gemm_pingpong(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny-M kernel: weight streaming with in-workgroup split-K.
+//
+// For a few rows of A against many rows of B (the quantised LLM projection
+// at 16 tokens) the time goes into streaming B from HBM once; the MFMA work
+// is small.  A workgroup owns 32*MB rows x 32 columns of C and its WAVES
+// waves split K: wave w sums the 128-byte K-blocks [w*n/WAVES, (w+1)*n/WAVES).
+// Operands go straight from global memory into MFMA-shaped registers
+// (16-byte buffer loads; out-of-range rows, the K tail and blocks past the
+// wave's share read as zero without touching memory).  A wave issues the
+// loads of CHUNK blocks at once and then contracts them, so that a whole
+// share costs one memory round trip rather than one per block.  Lane l holds
+// row l % 32 and reads bytes 64*(l/32) .. +63 of each 128-byte block of that
+// row, four 16-byte pieces that serve four MFMA K-steps (eight 8-byte pieces
+// for packed int4); A and B use the same byte-to-step assignment, so the sum
+// over k is unchanged, and the two half-waves cover each 128-byte row
+// segment.  The partial sums are combined through LDS in a fixed wave order
+// and the epilogue is applied once per output element.
+template <int KIND, int MB, int WAVES, int CHUNK>
+__global__ __launch_bounds__(WAVES * 64) void gemm_skinny(GemmArgs p) {
+  using Acc = typename KindTraits<KIND>::Acc;
+  constexpr bool I4 = KIND == KIND_I4;
+  constexpr int kBlock = 128;
+  constexpr int MT = 32 * MB, NT = 32;
+  constexpr int kThreads = WAVES * 64;
+  constexpr int kPitch = NT + 1;   // 32-bit words per reduction row
+
+  __shared__ __attribute__((aligned(16))) uint32_t red[WAVES * MT * kPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tm = blockIdx.x / p.tiles_n, tn = blockIdx.x % p.tiles_n;
+  const int m0 = tm * MT, n0 = tn * NT;
+  const int rows_a = min(MT, p.M - m0);
+  const int rows_b = min(NT, p.N - n0);
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.A + (size_t)m0 * p.row_bytes), 0, rows_a * p.row_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.B + (size_t)n0 * p.row_bytes), 0, rows_b * p.row_bytes, kBufferWord3);
+
+  const int r = lane & 31, h = lane >> 5;
+  const int nblk = p.k_stages;
+  const int b0 = (int)(((long long)nblk * wave) / WAVES);
+  const int b1 = (int)(((long long)nblk * (wave + 1)) / WAVES);
+
+  // Row offsets are fixed per lane; the K position only adds to them, and
+  // the range check is a select, so no branches surround the loads.
+  uint32_t a_row[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) a_row[mb] = (uint32_t)(mb * 32 + r) * (uint32_t)p.row_bytes;
+  const uint32_t b_row = (uint32_t)r * (uint32_t)p.row_bytes;
+  const uint32_t row_bytes = (uint32_t)p.row_bytes;
+
+  i32x4 fa[CHUNK][MB][4], fb[CHUNK][4];
+  auto load_block = [&](int blk, i32x4 (&a)[MB][4], i32x4 (&b)[4]) {
+    const uint32_t col0 = (uint32_t)blk * kBlock + (uint32_t)h * 64;
+    const bool in_range = blk < b1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t col = col0 + q * 16;
+      const bool ok = in_range && col < row_bytes;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        a[mb][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, ok ? a_row[mb] + col : kOutOfRange, 0, 0);
+      b[q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, ok ? b_row + col : kOutOfRange, 0, 0);
+    }
+  };
+
+  Acc acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[mb][e] = 0;
+
+  auto compute_block = [&](const i32x4 (&a)[MB][4], const i32x4 (&b)[4]) {
+    if constexpr (I4) {
+      // 64 packed bytes = 8 K-steps of 8 bytes (16 nibbles) each
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint32_t blo, bhi, blo1, bhi1;
+          expand_int4((uint32_t)b[q][2 * half], blo, bhi);
+          expand_int4((uint32_t)b[q][2 * half + 1], blo1, bhi1);
+          const i32x4 bv = {(int)blo, (int)bhi, (int)blo1, (int)bhi1};
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            uint32_t alo, ahi, alo1, ahi1;
+            expand_int4((uint32_t)a[mb][q][2 * half], alo, ahi);
+            expand_int4((uint32_t)a[mb][q][2 * half + 1], alo1, ahi1);
+            const i32x4 av = {(int)alo, (int)ahi, (int)alo1, (int)ahi1};
+            acc[mb] = mfma<KIND>(av, bv, acc[mb]);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma<KIND>(a[mb][q], b[q], acc[mb]);
+    }
+  };
+
+  for (int c = b0; c < b1; c += CHUNK) {
+#pragma unroll
+    for (int j = 0; j < CHUNK; ++j) load_block(c + j, fa[j], fb[j]);
+    // keep every load of the chunk ahead of the MFMAs (the scheduler would
+    // otherwise trade memory parallelism for registers)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < CHUNK; ++j) compute_block(fa[j], fb[j]);
+  }
+
+  // partial sums -> LDS (element e of lane l: row 8*(e/4) + 4*(l/32) + e%4,
+  // column l%32 of a 32x32 block)
+  uint32_t* mine = red + wave * MT * kPitch;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rr = mb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+      // copy the element out first: bit-casting a vector-element lvalue
+      // directly reads the vector's first element
+      const auto v = acc[mb][e];
+      mine[rr * kPitch + r] = __builtin_bit_cast(uint32_t, v);
+    }
+  __syncthreads();
+  for (int idx = tid; idx < MT * NT; idx += kThreads) {
+    const int rr = idx / NT, cc = idx % NT;
+    const int row = m0 + rr, col = n0 + cc;
+    if (row >= p.M || col >= p.N) continue;
+    if constexpr (KIND == KIND_F16) {
+      float sum = 0.f;
+      for (int w = 0; w < WAVES; ++w) sum += __builtin_bit_cast(float, red[(w * MT + rr) * kPitch + cc]);
+      ((float*)p.C)[(size_t)row * p.N + col] = sum;
+    } else {
+      int32_t sum = 0;
+      for (int w = 0; w < WAVES; ++w) sum += (int32_t)red[(w * MT + rr) * kPitch + cc];
+      if constexpr (KIND == KIND_I4) {
+        ((int32_t*)p.C)[(size_t)row * p.N + col] = sum >> 8;   // undo the 16 x 16 scaling
+      } else if constexpr (KIND == KIND_I8_DEQUANT) {
+        float t = (float)sum;
+        t = t * p.row_scale[row];
+        t = t * p.col_scale[col];
+        ((float*)p.C)[(size_t)row * p.N + col] = t;
+      } else {
+        ((int32_t*)p.C)[(size_t)row * p.N + col] = sum;
+      }
+    }
+  }
+}
+
 }  // namespace lpgemm

@@ -93,7 +93,10 @@ enum KernelCfg {
   CFG_V1_128x128 = 5,    // 4 waves, 64 x 64 per wave, register-staged loads
   CFG_V1_64x64 = 6,      // 4 waves, 32 x 32 per wave, register-staged loads
   CFG_PP_R64 = 7,        // 8 waves ping-pong, 256 x 256, 4 stages of 64-byte rows
-  CFG_COUNT = 8
+  CFG_SKINNY_32 = 8,     // 32 x 32 tiles, 8 waves split K, 4 K-blocks per load round
+  CFG_SKINNY_64 = 9,     // 64 x 32 tiles, 8 waves split K, 2 K-blocks per load round
+  CFG_SKINNY_32_W16 = 10,  // 32 x 32 tiles, 16 waves split K, 2 K-blocks per load round
+  CFG_COUNT = 11
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -103,6 +106,7 @@ int stage_row_bytes(KernelCfg c) {
                                                                                                  : 128;
 }
 bool expands_int4_in_lds(KernelCfg c) { return c >= CFG_V1_256x256 && c <= CFG_V1_64x64; }
+bool is_skinny(KernelCfg c) { return c >= CFG_SKINNY_32 && c <= CFG_SKINNY_32_W16; }
 
 int tiles(int64_t x, int t) { return (int)((x + t - 1) / t); }
 
@@ -120,6 +124,10 @@ int forced_config() {
 KernelCfg choose_config(int64_t M, int64_t N, int cu_count) {
   const int f = forced_config();
   if (f >= 0) return (KernelCfg)f;
+  // few rows against many columns: stream B with split-K workgroups
+  if (M <= 32) return CFG_SKINNY_32;
+  if (M <= 64) return CFG_SKINNY_64;
+  if (M <= 128) return CFG_128_S4_R64;
   const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
   if (big >= cu_count) return CFG_256_S2_R128;
   const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
@@ -162,6 +170,7 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
 
   const KernelCfg cfg = choose_config(M, N, dev.cu_count);
   const int64_t stage_bytes = (KIND == KIND_I4 && expands_int4_in_lds(cfg)) ? K : row_bytes;
+  (void)is_skinny;
   const int rowb = stage_row_bytes(cfg);
   args.k_stages = (int)((stage_bytes + rowb - 1) / rowb);
 
@@ -180,6 +189,12 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<128, 128>((const void*)&gemm_tiled<KIND, 128, 128, 2, 2>, args, 256, stream);
     case CFG_PP_R64:
       return launch<256, 256>((const void*)&gemm_pingpong<KIND, 64>, args, 512, stream);
+    case CFG_SKINNY_32:
+      return launch<32, 32>((const void*)&gemm_skinny<KIND, 1, 8, 4>, args, 512, stream);
+    case CFG_SKINNY_64:
+      return launch<64, 32>((const void*)&gemm_skinny<KIND, 2, 8, 2>, args, 512, stream);
+    case CFG_SKINNY_32_W16:
+      return launch<32, 32>((const void*)&gemm_skinny<KIND, 1, 16, 2>, args, 1024, stream);
     default:
       return launch<64, 64>((const void*)&gemm_tiled<KIND, 64, 64, 2, 2>, args, 256, stream);
   }

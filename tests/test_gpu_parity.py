@@ -177,9 +177,11 @@ def test_dequant_llm_2048_sampled():
 
 # ---------------------------------------------------------------- ragged shapes
 
-# (M, N) pairs that select the 64x64, 128x128 and 256x256 tile configurations
-# on a 256-CU device, none of them tile multiples
-RAGGED_MN = [(1, 1), (33, 47), (257, 300), (1500, 1380), (4100, 4100)]
+# (M, N) pairs that select, on a 256-CU device, the skinny split-K kernels
+# (M <= 32, M <= 64), the 128 x 128 kernel (M <= 128, and 1500 x 1380), the
+# 64 x 64 kernel (257 x 300) and the 256 x 256 kernel (4100 x 4100); none of
+# them are tile multiples
+RAGGED_MN = [(1, 1), (33, 47), (64, 96), (100, 700), (257, 300), (1500, 1380), (4100, 4100)]
 
 
 @pytest.mark.parametrize("M,N", RAGGED_MN)
@@ -327,3 +329,43 @@ def test_back_to_back_launches():
         ref = oracle.gemm_i8(p.a, p.b_t)
         for r in range(3):
             np.testing.assert_array_equal(outs[3 * i + r].cpu().numpy(), ref)
+
+
+def test_graph_replays_match_eager():
+    # captured launches replayed several times, with eager work and
+    # synchronisation between replays, must reproduce the eager results
+    _say("graph capture")
+    p8 = inputs.int8_problem(300, 520, 400, 77, scales=True)
+    p4 = inputs.int4_problem(40, 700, 256, 78)
+    ph = inputs.f16_problem(520, 300, 200, 79)
+    a8, b8, rs, cs = _dev(p8.a), _dev(p8.b_t), _dev(p8.row_scale), _dev(p8.col_scale)
+    a4, b4 = _dev(p4.a_packed), _dev(p4.b_packed)
+    ah, bh = _dev(ph.a), _dev(ph.b_t)
+    eager = [lp.gemm_i8(a8, b8), lp.gemm_i8_dequant(a8, b8, rs, cs), lp.gemm_i4(a4, b4, 256),
+             lp.gemm_f16(ah, bh)]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(e) for e in eager]
+    # warm up on a side stream before capture, as torch requires
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lp.gemm_i8(a8, b8, out=outs[0])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lp.gemm_i8(a8, b8, out=outs[0])
+        lp.gemm_i8_dequant(a8, b8, rs, cs, out=outs[1])
+        lp.gemm_i4(a4, b4, 256, out=outs[2])
+        lp.gemm_f16(ah, bh, out=outs[3])
+    for rep in range(4):
+        for o in outs:
+            o.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, o in zip(eager, outs):
+            assert torch.equal(e.view(torch.int32), o.view(torch.int32)), rep
+        lp.gemm_i8(a8, b8)   # eager work between replays
+        torch.cuda.synchronize()
+    np.testing.assert_array_equal(outs[0].cpu().numpy(), oracle.gemm_i8(p8.a, p8.b_t))

@@ -50,25 +50,29 @@ def build(force: bool = True) -> str:
 _lib = None
 
 
+def _configure(lib):
+    """Declare the argument and result types of the oracle entry points."""
+    for name in ("oracle_i8", "oracle_i4"):
+        f = getattr(lib, name)
+        f.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i64, _i64]
+        f.restype = ctypes.c_int
+    lib.oracle_f16.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i64, _i64]
+    lib.oracle_f16.restype = ctypes.c_int
+    lib.oracle_i8_dequant.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _i64]
+    lib.oracle_i8_dequant.restype = ctypes.c_int
+    lib.oracle_f16_decode.argtypes = [ctypes.c_uint16, ctypes.POINTER(ctypes.c_int)]
+    lib.oracle_f16_decode.restype = ctypes.c_double
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
             build()
-        lib = ctypes.CDLL(_LIB)
-        for name in ("oracle_i8", "oracle_i4"):
-            f = getattr(lib, name)
-            f.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i64, _i64]
-            f.restype = ctypes.c_int
-        lib.oracle_f16.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i64, _i64]
-        lib.oracle_f16.restype = ctypes.c_int
-        lib.oracle_i8_dequant.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _i64]
-        lib.oracle_i8_dequant.restype = ctypes.c_int
-        lib.oracle_f16_decode.argtypes = [ctypes.c_uint16, ctypes.POINTER(ctypes.c_int)]
-        lib.oracle_f16_decode.restype = ctypes.c_double
-        lib.oracle_num_threads.argtypes = []
-        lib.oracle_num_threads.restype = ctypes.c_int
-        _lib = lib
+        _lib = _configure(ctypes.CDLL(_LIB))
     return _lib
 
 

@@ -50,3 +50,18 @@ def test_dequant_worked():
     out = oracle.gemm_i8_dequant(A, B_t, np.array(d["row_scale"], np.float32),
                                  np.array(d["col_scale"], np.float32))
     assert out.tolist() == _vals(d["out"])
+
+
+def test_dequant_two_roundings():
+    # fixtures where two binary32 roundings differ from one (exact derivation
+    # in tests/golden/make_dequant_rounding.py)
+    G2 = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "dequant_rounding.json")))
+    for case in G2["cases"]:
+        A = np.array([case["a_row"]], np.int8)
+        B_t = np.array([case["b_col"]], np.int8)
+        assert int(oracle.gemm_i8(A, B_t)[0, 0]) == case["acc"]
+        rs = np.array([int(case["row_scale_bits"], 16)], np.uint32).view(np.float32)
+        cs = np.array([int(case["col_scale_bits"], 16)], np.uint32).view(np.float32)
+        out = oracle.gemm_i8_dequant(A, B_t, rs, cs)
+        assert int(out.view(np.uint32)[0, 0]) == int(case["expected_bits"], 16)
+        assert case["expected_bits"] != case["single_rounding_bits"]

@@ -49,16 +49,3 @@ def test_scale_index_orientation():
     for i in range(M):
         for j in range(N):
             assert out[i, j] == np.float32(np.float32(16.0 * rs[i]) * cs[j])
-
-
-def test_fp32_rounding_steps():
-    # acc = 3, rs = 1/3 rounded to fp32, cs = 3: the two roundings leave the
-    # binary32 value of fl(fl(3 * fl(1/3)) * 3), not 3.
-    A = np.ones((1, 16), np.int8)
-    B_t = np.zeros((1, 16), np.int8)
-    B_t[0, :3] = 1
-    rs = np.array([1.0 / 3.0], np.float32)
-    cs = np.array([3.0], np.float32)
-    out = oracle.gemm_i8_dequant(A, B_t, rs, cs)
-    step1 = np.float32(np.float32(3.0) * rs[0])
-    assert out[0, 0] == np.float32(step1 * cs[0])

@@ -31,10 +31,13 @@ __global__ __launch_bounds__(256) void mfma_i8(int iters, int* out, unsigned see
     b[i] = {(int)x, (int)(x * 5u), (int)(x * 9u), (int)(x * 13u)};
   }
   i32x16 c[kChains] = {};
-  for (int it = 0; it < iters; ++it) {
+  // the operand rotation is unrolled so every register index is static
+  for (int it = 0; it < iters; it += 4) {
 #pragma unroll
-    for (int j = 0; j < kChains; ++j)
-      c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[j & 3], b[(j + it) & 3], c[j], 0, 0, 0);
+    for (int rot = 0; rot < 4; ++rot)
+#pragma unroll
+      for (int j = 0; j < kChains; ++j)
+        c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[j & 3], b[(j + rot) & 3], c[j], 0, 0, 0);
   }
   int s = 0;
   for (int j = 0; j < kChains; ++j)
@@ -53,10 +56,12 @@ __global__ __launch_bounds__(256) void mfma_f16(int iters, int* out, unsigned se
       b[i][e] = (_Float16)(float)(((t * 11 + i * 3 + e * 7) % 17) - 8) * (_Float16)0.125f;
     }
   f32x16 c[kChains] = {};
-  for (int it = 0; it < iters; ++it) {
+  for (int it = 0; it < iters; it += 4) {
 #pragma unroll
-    for (int j = 0; j < kChains; ++j)
-      c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j & 3], b[(j + it) & 3], c[j], 0, 0, 0);
+    for (int rot = 0; rot < 4; ++rot)
+#pragma unroll
+      for (int j = 0; j < kChains; ++j)
+        c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j & 3], b[(j + rot) & 3], c[j], 0, 0, 0);
   }
   float s = 0;
   for (int j = 0; j < kChains; ++j)
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(256) void mfma_f16(int iters, int* out, unsigned se
 template <typename Kernel>
 double sustained(Kernel k, double seconds, double macs_per_wave_iter, int cus, int* out) {
   const int blocks = cus * 2;   // 256 threads each: two waves per SIMD
-  const int iters = 20000;
+  const int iters = 20000;   // a multiple of 4
   hipEvent_t e0, e1;
   (void)hipEventCreate(&e0);
   (void)hipEventCreate(&e1);

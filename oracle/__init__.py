@@ -62,6 +62,8 @@ def _configure(lib):
     lib.oracle_i8_dequant.restype = ctypes.c_int
     lib.oracle_f16_decode.argtypes = [ctypes.c_uint16, ctypes.POINTER(ctypes.c_int)]
     lib.oracle_f16_decode.restype = ctypes.c_double
+    lib.oracle_quantize_rows_f16.argtypes = [_i64, _i64, _p, _p, _p, _i64, _i64]
+    lib.oracle_quantize_rows_f16.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -179,6 +181,25 @@ def gemm_i8_dequant(A: np.ndarray, B_t: np.ndarray, row_scale: np.ndarray,
                                                          _ptr(rs), _ptr(cs), *a),
                        M, N, rows, [np.float32])
     return out
+
+
+def quantize_rows_f16(X: np.ndarray, rows=None):
+    """Per-row int8 quantisation of fp16 X (M x K): returns (Q int8 M x K,
+    scale float32 M) with scale = absmax / 127 and Q = nearest-even integer to
+    x / scale, both in binary32, clamped to [-127, 127]."""
+    X = _c(X, np.float16).view(np.uint16)
+    M, K = X.shape
+    lib = _load()
+    qs, ss = [], []
+    for b, e in _row_runs(rows, M):
+        q = np.empty((e - b, K), np.int8)
+        sc = np.empty(e - b, np.float32)
+        _check(lib.oracle_quantize_rows_f16(M, K, _ptr(X), _ptr(q), _ptr(sc), b, e))
+        qs.append(q)
+        ss.append(sc)
+    if not qs:
+        return np.empty((0, K), np.int8), np.empty(0, np.float32)
+    return np.concatenate(qs, axis=0), np.concatenate(ss)
 
 
 def f16_decode(bits: int):

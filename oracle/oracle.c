@@ -23,6 +23,13 @@
  *                   normaliser of the relative-error metric).
  *   dequant       : s from the int8 path, then in binary32, left to right:
  *                   t = (float)s; t = t * rs[i]; t = t * cs[j].
+ *   quantise      : per-row symmetric int8 quantisation of fp16 activations,
+ *                   the step in front of a W8A8 projection (the pages leave
+ *                   the rule open; this is the plainest reading): absmax =
+ *                   max |x|, scale = absmax / 127 in binary32, q = the
+ *                   nearest-even integer to x / scale computed in binary32,
+ *                   clamped to [-127, 127]; an all-zero row gets scale 0 and
+ *                   q = 0.
  *
  * Layouts: A is M x K row-major; B is stored K-contiguous (N rows of K);
  * C is M x N row-major.  Every entry point computes the output rows
@@ -192,6 +199,51 @@ int oracle_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A, const in
             t = t * row_scale[i];
             t = t * col_scale[j];
             out[(i - row_begin) * N + j] = t;
+        }
+    }
+    return status;
+}
+
+/* Per-row int8 quantisation of fp16 rows (see the header comment).
+ * X: M x K binary16 bits; Q: (row_end-row_begin) x K int8; scale: one float
+ * per computed row.  Division and rounding are binary32, round to nearest
+ * even (SSE arithmetic, FLT_EVAL_METHOD == 0). */
+int oracle_quantize_rows_f16(int64_t M, int64_t K, const uint16_t *X, int8_t *Q, float *scale,
+                             int64_t row_begin, int64_t row_end)
+{
+    if (bad_range(M, row_begin, row_end))
+        return ORACLE_BAD_RANGE;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = row_begin; i < row_end; ++i) {
+        double amax = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            int fin;
+            double v = oracle_f16_decode(X[i * K + k], &fin);
+            if (!fin) {
+#pragma omp atomic write
+                status = ORACLE_NONFINITE;
+            }
+            if (fabs(v) > amax)
+                amax = fabs(v);
+        }
+        /* amax is a binary16 value, so the conversion is exact */
+        volatile float s = (float)amax / 127.0f;
+        scale[i - row_begin] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            int fin;
+            float v = (float)oracle_f16_decode(X[i * K + k], &fin);
+            int8_t q = 0;
+            if (s != 0.0f) {
+                volatile float t = v / s;
+                float r = rintf(t);
+                if (r > 127.0f)
+                    r = 127.0f;
+                if (r < -127.0f)
+                    r = -127.0f;
+                q = (int8_t)r;
+            }
+            Q[(i - row_begin) * K + k] = q;
         }
     }
     return status;

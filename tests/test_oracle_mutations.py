@@ -21,6 +21,7 @@ import test_oracle_dequant as t_dq
 import test_oracle_f16 as t_f16
 import test_oracle_int4 as t_i4
 import test_oracle_int8 as t_i8
+import test_oracle_quant as t_qz
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -45,6 +46,9 @@ MUTATIONS = {
     "f16_den_without_abs": ("d += fabs(a) * fabs(b);", "d += a * b;"),
     "f16_float_accumulator": ("double s = 0.0, d = 0.0;", "float s = 0.0f; double d = 0.0;"),
     "dq_missing_col_scale": ("t = t * col_scale[j];", "t = t * 1.0f;"),
+    "qz_divide_by_128": ("volatile float s = (float)amax / 127.0f;", "volatile float s = (float)amax / 128.0f;"),
+    "qz_round_half_away": ("float r = rintf(t);", "float r = roundf(t);"),
+    "qz_reciprocal_multiply": ("volatile float t = v / s;", "volatile float t = v * (1.0f / s);"),
     "dq_single_rounding": ("volatile float t = (float)(int32_t)s;\n            t = t * row_scale[i];\n            t = t * col_scale[j];",
                            "volatile float t = (float)((double)(int32_t)s * row_scale[i] * col_scale[j]);"),
 }
@@ -61,6 +65,9 @@ PINS = {
             lambda: t_f16.test_integer_valued_equals_int_oracle(7, 9, 16),
             lambda: t_f16.test_exact_rational_bound(2, 3, 64, 100.0), t_f16.test_subnormal_and_signs,
             test_golden.test_fp16_worked],
+    "qz": [lambda: t_qz.test_exact_rational(6, 64, 1.0), lambda: t_qz.test_exact_rational(4, 200, 30.0),
+           t_qz.test_integer_row_with_127_is_identity, t_qz.test_zero_row, t_qz.test_ties_to_even,
+           t_qz.test_extremes_map_to_127, t_qz.test_reconstruction_bound, t_qz.test_tie_fixtures],
     "dq": [t_dq.test_power_of_two_scales_exact, lambda: t_dq.test_three_rounding_bound(33, 7, 512),
            t_dq.test_scale_index_orientation, test_golden.test_dequant_worked,
            test_golden.test_dequant_two_roundings],

@@ -38,10 +38,10 @@ if ROOT not in sys.path:
 METRIC = "INT8/INT4 TOPS and FP16 TFLOPS at N=8192 on 1 MI355X; % of MFMA peak"
 # Dense MFMA peaks of the MI355X (256 CUs, 2.4 GHz): int8 8192 ops and fp16
 # 4096 flops per CU per clock.  INT4 runs on the int8 MFMA.
-PEAK_TOPS = {"i8": 5033.2, "i4": 5033.2, "dq": 5033.2, "f16": 2516.6}
+PEAK_TOPS = {"i8": 5033.2, "i4": 5033.2, "dq": 5033.2, "w8": 5033.2, "f16": 2516.6}
 HBM_PEAK_GBS = 8000.0
-UNIT = {"i8": "TOPS", "i4": "TOPS", "dq": "TOPS", "f16": "TFLOPS"}
-DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "f16": "f16"}
+UNIT = {"i8": "TOPS", "i4": "TOPS", "dq": "TOPS", "w8": "TOPS", "f16": "TFLOPS"}
+DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "w8": "i8", "f16": "f16"}
 KERNEL_SOURCES = ["precision_dense_gemm_02_amd/csrc/gemm_kernels.hpp",
                   "precision_dense_gemm_02_amd/csrc/lpgemm.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -61,6 +61,9 @@ def parse_workload(name: str):
     if kind == "llm":
         from precision_dense_gemm_02_amd import inputs
         return "dq", size, inputs.LLM_N, inputs.LLM_K
+    if kind == "w8a8":
+        from precision_dense_gemm_02_amd import inputs
+        return "w8", size, inputs.LLM_N, inputs.LLM_K
     if kind not in ("i8", "i4", "f16"):
         raise SystemExit(f"unknown workload {name}")
     return kind, size, size, size
@@ -112,6 +115,25 @@ class Workload:
             self.launch = lambda i: lp.gemm_f16(a, b, out=out)
             self.in_bytes = 2 * (M * K + N * K)
             self.out_bytes = 4 * M * N
+        elif kind == "w8":
+            # fp16 activations quantised per row, then the dequantising GEMM:
+            # two launches per step
+            self.seed = inputs.seed_for("w8a8", M)
+            p = inputs.w8a8_problem(M, N, K, self.seed)
+            self.host = p
+            x, ws = to(p.x), to(p.w_scale)
+            copies = max(1, -(-336 * 2 ** 20 // (N * K)))
+            ws_list = [to(p.w) for _ in range(copies)]
+            q = torch.empty((M, K), dtype=torch.int8, device=dev)
+            s = torch.empty((M,), dtype=torch.float32, device=dev)
+            out = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+            def step(i):
+                lp.quantize_rows_f16(x, q_out=q, scale_out=s)
+                lp.gemm_i8_dequant(q, ws_list[i % len(ws_list)], s, ws, out=out)
+            self.launch = step
+            self.in_bytes = 2 * M * K + N * K + 4 * N
+            self.out_bytes = 4 * M * N
         else:  # dequantised LLM projection
             self.seed = inputs.seed_for("llm", M)
             p = inputs.llm_problem(M, self.seed)
@@ -145,6 +167,10 @@ class Workload:
             e = oracle.f16_rel_error(got, ref, den)
             return f"max_rel_err {e['max_rel']:.3e} over {len(rows)} rows (tol 1e-3)" \
                 if e["max_rel"] <= 1e-3 else f"FAIL max_rel_err {e['max_rel']:.3e}"
+        elif self.kind == "w8":
+            q, s = oracle.quantize_rows_f16(p.x, rows=rows)
+            ref = oracle.gemm_i8_dequant(q, p.w, s, p.w_scale)
+            ok = np.array_equal(got.view(np.uint32), ref.view(np.uint32))
         else:
             ref = oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale, rows=rows)
             ok = np.array_equal(got.view(np.uint32), ref.view(np.uint32))
@@ -243,6 +269,9 @@ def cpu_baseline(w: Workload, seconds: float) -> dict:
             oracle.gemm_i4(p.a_packed, p.b_packed, w.K, rows=rows)
         elif w.kind == "f16":
             oracle.gemm_f16(p.a, p.b_t, rows=rows)
+        elif w.kind == "w8":
+            q, s = oracle.quantize_rows_f16(p.x, rows=rows)
+            oracle.gemm_i8_dequant(q, p.w, s, p.w_scale)
         else:
             oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale, rows=rows)
         return time.perf_counter() - t0
@@ -273,6 +302,9 @@ def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
            "kernel_ms_min": round(t["kernel_ms_min"], 5),
            "pct_mfma_peak": round(100 * value / PEAK_TOPS[w.kind], 2),
            "roofline": r, "parity": w.check_sampled()}
+    if w.kind == "w8":
+        rec["note"] = ("one step is two launches (per-row quantise, then the dequantising "
+                       "GEMM); the kernel time and roofline cover both")
     return w, rec
 
 

@@ -110,6 +110,25 @@ lpgemm_status lpgemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A
                                 const int8_t *B, const float *row_scale,
                                 const float *col_scale, float *C, hipStream_t stream);
 
+/* Largest K of lpgemm_quantize_rows_f16 (byte offsets within a row of X then
+ * fit easily in the 32-bit offsets the kernels use). */
+#define LPGEMM_MAX_K_QUANT 1048576
+
+/* Per-row int8 quantisation of fp16 activations, the step in front of a W8A8
+ * projection that lpgemm_i8_dequant then computes (the PTX-vs-WMMA summary
+ * page's closing advice on quantised LLM inference; the pages leave the
+ * quantisation rule open, and this is its plainest form):
+ *   row_scale[i] = max_k |X[i][k]| / 127, in binary32;
+ *   Q[i][k] = the nearest-even integer to X[i][k] / row_scale[i], in binary32,
+ *             clamped to [-127, 127];  an all-zero row gets scale 0 and Q 0.
+ * X: M x K binary16, row-major; Q: M x K int8; row_scale: M floats.
+ * K must be a multiple of 8 and at most LPGEMM_MAX_K_QUANT.  X and Q must be
+ * 16-byte aligned, row_scale 4-byte aligned; X and Q may be NULL when K = 0.
+ * M = 0 is a no-op.  Errors as for the GEMM entry points; inf/NaN inputs are
+ * outside the contract. */
+lpgemm_status lpgemm_quantize_rows_f16(int64_t M, int64_t K, const void *X, int8_t *Q,
+                                       float *row_scale, hipStream_t stream);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char *lpgemm_status_string(lpgemm_status status);
 

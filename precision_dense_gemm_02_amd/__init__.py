@@ -7,7 +7,7 @@ include/lpgemm.h; this package is the torch-facing binding (see _binding.py),
 the in-tree build step (build.py) and the seeded input generators (inputs.py).
 """
 from ._binding import (LpgemmError, gemm_f16, gemm_i4, gemm_i8, gemm_i8_dequant,  # noqa: F401
-                       load_library, status_string, version)
+                       load_library, quantize_rows_f16, status_string, version, w8a8_linear)
 
 __all__ = ["LpgemmError", "gemm_i8", "gemm_i4", "gemm_f16", "gemm_i8_dequant",
-           "load_library", "status_string", "version"]
+           "quantize_rows_f16", "w8a8_linear", "load_library", "status_string", "version"]

@@ -27,6 +27,7 @@ LPGEMM_ERROR_LAUNCH = 5
 
 MAX_K_INT = 131071
 MAX_K_F16 = 1048576
+MAX_K_QUANT = 1048576
 
 
 class LpgemmError(RuntimeError):
@@ -58,6 +59,8 @@ def load_library():
             f.restype = ctypes.c_int
         lib.lpgemm_i8_dequant.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p]
         lib.lpgemm_i8_dequant.restype = ctypes.c_int
+        lib.lpgemm_quantize_rows_f16.argtypes = [_i64, _i64, _p, _p, _p, _p]
+        lib.lpgemm_quantize_rows_f16.restype = ctypes.c_int
         lib.lpgemm_status_string.argtypes = [ctypes.c_int]
         lib.lpgemm_status_string.restype = ctypes.c_char_p
         lib.lpgemm_version.argtypes = []
@@ -209,3 +212,32 @@ def gemm_i8_dequant(a, b_t, row_scale, col_scale, out=None):
                                                 out.data_ptr(), _stream_handle(dev)),
                "lpgemm_i8_dequant")
     return out
+
+
+def quantize_rows_f16(x, q_out=None, scale_out=None):
+    """Per-row int8 quantisation of fp16 x (M x K): returns (q int8 M x K,
+    scale fp32 M) with scale = absmax / 127 and q = nearest-even integer to
+    x / scale (binary32), clamped to [-127, 127]."""
+    torch = _torch()
+    _operand(x, torch.float16, "x")
+    dev = x.device
+    M, K = x.shape
+    q_out = _output(q_out, (M, K), torch.int8, dev)
+    if scale_out is None:
+        scale_out = torch.empty((M,), dtype=torch.float32, device=dev)
+    elif scale_out.dtype != torch.float32 or tuple(scale_out.shape) != (M,) or not scale_out.is_contiguous():
+        raise ValueError(f"scale_out must be a contiguous fp32 vector of length {M}")
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_quantize_rows_f16(M, K, x.data_ptr(), q_out.data_ptr(),
+                                                       scale_out.data_ptr(), _stream_handle(dev)),
+               "lpgemm_quantize_rows_f16")
+    return q_out, scale_out
+
+
+def w8a8_linear(x, w, w_scale, out=None):
+    """fp32 y = dequant(quantize(x) . w): x fp16 M x K activations, w int8
+    N x K weights (K-contiguous), w_scale fp32 per output column.  Two library
+    calls on the current stream: lpgemm_quantize_rows_f16 (into buffers this
+    function allocates) and lpgemm_i8_dequant."""
+    q, s = quantize_rows_f16(x)
+    return gemm_i8_dequant(q, w, s, w_scale, out=out)

@@ -1046,4 +1046,116 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-row int8 quantisation of fp16 activations (the step in front of a W8A8
+// projection): scale s = absmax / 127 and q = the nearest-even integer to the
+// binary32 quotient x / s, clamped to [-127, 127]; an all-zero row gets
+// s = 0 and q = 0.  The max is exact, so the order of the absmax reduction
+// does not matter.  HBM-bound: 2K bytes read and K + 4 bytes written per row.
+//
+// The quotient.  s is always RN(a / 127) for a finite fp16 a, so only about
+// 31.7 thousand scales occur.  For every one of them and every finite fp16 x
+// the sequence  r = RN(1 / s) (once per row), q0 = RN(x r),
+// e = fma(-q0, s, x), q = RN(e r + q0)  gives exactly RN(x / s) (checked
+// exhaustively on the CPU, over all 2.0e9 pairs); this is the residual
+// correction step of Markstein's division, and it costs three instructions
+// per element where a full IEEE division costs about ten.
+
+// Eight fp16 values to eight int8 codes, packed little-endian.  s must be
+// nonzero and r = RN(1 / s).
+__device__ __forceinline__ uint64_t quantize8(f16x8 h, float s, float r) {
+  uint64_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = (float)h[e];
+    const float q0 = __fmul_rn(x, r);
+    const float q = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
+    const float c = fminf(fmaxf(rintf(q), -127.f), 127.f);
+    packed |= (uint64_t)(uint8_t)(int8_t)(int)c << (8 * e);
+  }
+  return packed;
+}
+
+__device__ __forceinline__ float absmax8(f16x8 h, float amax) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)h[e]));
+  return amax;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// Rows of at most 512 * WPR * NC halves, held in registers: WPR wavefronts
+// share a row (a workgroup of four waves takes 4 / WPR rows) and each lane
+// keeps its NC 16-byte chunks (chunk li + 64 WPR c, li the lane's index
+// within the row), so the row is read once for both passes.  Chunks past the
+// row end load as zero through the buffer resource, which leaves the absmax
+// unchanged.  WPR = 4 spreads a row over 256 lanes for short M (the rounding
+// pass is ALU latency there); WPR = 1 needs no LDS and no barrier.
+template <int WPR, int NC>
+__global__ __launch_bounds__(256) void quantize_rows_f16_regs(const uint8_t* __restrict__ X,
+                                                              int8_t* __restrict__ Q,
+                                                              float* __restrict__ scale, int M,
+                                                              int K) {
+  static_assert(WPR == 1 || WPR == 4, "a row takes one wave or the whole workgroup");
+  constexpr int kRowLanes = 64 * WPR;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * (4 / WPR) + wave / WPR;
+  const int li = threadIdx.x - (wave / WPR) * kRowLanes;
+  if (WPR == 1 && row >= M) return;   // with WPR = 4 the grid has exactly M workgroups
+  const int chunks = K >> 3;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + (size_t)row * K * 2), 0, K * 2, kBufferWord3);
+  i32x4 v[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    v[c] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)(li + kRowLanes * c) * 16u, 0, 0);
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) amax = absmax8(__builtin_bit_cast(f16x8, v[c]), amax);
+  amax = wave_max(amax);
+  if constexpr (WPR > 1) {
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  }
+  const float s = __fdiv_rn(amax, 127.0f);
+  if (li == 0) scale[row] = s;
+  const float r = __fdiv_rn(1.0f, s);
+  uint64_t* qrow = (uint64_t*)(Q + (size_t)row * K);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int idx = li + kRowLanes * c;
+    if (idx < chunks) qrow[idx] = s != 0.f ? quantize8(__builtin_bit_cast(f16x8, v[c]), s, r) : 0;
+  }
+}
+
+// Longer rows (and K = 0): one workgroup per row and two passes over it, the
+// second re-reading the row (mostly from L2).
+__global__ __launch_bounds__(256) void quantize_rows_f16(const uint8_t* __restrict__ X,
+                                                         int8_t* __restrict__ Q,
+                                                         float* __restrict__ scale, int K) {
+  const int row = blockIdx.x;
+  const int chunks = K / 8;   // 16-byte chunks of 8 halves
+  const i32x4* xrow = (const i32x4*)(X + (size_t)row * K * 2);
+  float amax = 0.f;
+  for (int c = threadIdx.x; c < chunks; c += 256)
+    amax = absmax8(__builtin_bit_cast(f16x8, xrow[c]), amax);
+  amax = wave_max(amax);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  const float s = __fdiv_rn(amax, 127.0f);
+  if (threadIdx.x == 0) scale[row] = s;
+  const float r = __fdiv_rn(1.0f, s);
+  uint64_t* qrow = (uint64_t*)(Q + (size_t)row * K);
+  for (int c = threadIdx.x; c < chunks; c += 256)
+    qrow[c] = s != 0.f ? quantize8(__builtin_bit_cast(f16x8, xrow[c]), s, r) : 0;
+}
+
 }  // namespace lpgemm

@@ -228,6 +228,50 @@ lpgemm_status lpgemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t* A
   return run<KIND_I8_DEQUANT>(M, N, K, A, B, C, row_scale, col_scale, stream);
 }
 
+lpgemm_status lpgemm_quantize_rows_f16(int64_t M, int64_t K, const void* X, int8_t* Q,
+                                       float* row_scale, hipStream_t stream) {
+  if (M < 0 || K < 0 || M > INT32_MAX) return LPGEMM_ERROR_INVALID_VALUE;
+  if (K % 8 != 0 || K > LPGEMM_MAX_K_QUANT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  if (M == 0) return LPGEMM_SUCCESS;
+  if (!row_scale) return LPGEMM_ERROR_INVALID_VALUE;
+  if (K > 0 && (!X || !Q)) return LPGEMM_ERROR_INVALID_VALUE;
+  if (!aligned4(row_scale)) return LPGEMM_ERROR_MISALIGNED;
+  if (K > 0 && (!aligned16(X) || !aligned16(Q))) return LPGEMM_ERROR_MISALIGNED;
+  DeviceInfo dev;
+  lpgemm_status st = current_device(dev);
+  if (st != LPGEMM_SUCCESS) return st;
+  const uint8_t* x = static_cast<const uint8_t*>(X);
+  int m = (int)M, k = (int)K;
+  hipError_t e;
+  if (K > 0 && K <= 8192) {
+    // rows held in registers: a whole workgroup per row while there are
+    // fewer rows than SIMDs, one wavefront per row beyond that
+    const bool wide = M < 4 * (int64_t)dev.cu_count;
+    const int per_lane = (int)((K / 8 + (wide ? 255 : 63)) / (wide ? 256 : 64));
+    const void* fn;
+    if (wide) {
+      fn = per_lane <= 1 ? (const void*)&quantize_rows_f16_regs<4, 1>
+         : per_lane <= 2 ? (const void*)&quantize_rows_f16_regs<4, 2>
+                         : (const void*)&quantize_rows_f16_regs<4, 4>;
+    } else {
+      fn = per_lane <= 1 ? (const void*)&quantize_rows_f16_regs<1, 1>
+         : per_lane <= 2 ? (const void*)&quantize_rows_f16_regs<1, 2>
+         : per_lane <= 4 ? (const void*)&quantize_rows_f16_regs<1, 4>
+         : per_lane <= 8 ? (const void*)&quantize_rows_f16_regs<1, 8>
+                         : (const void*)&quantize_rows_f16_regs<1, 16>;
+    }
+    void* kargs[] = {&x, &Q, &row_scale, &m, &k};
+    const unsigned grid = wide ? (unsigned)M : (unsigned)((M + 3) / 4);
+    e = hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, stream);
+  } else {
+    // longer rows (and K = 0): one workgroup per row, two passes over it
+    void* kargs[] = {&x, &Q, &row_scale, &k};
+    e = hipLaunchKernel((const void*)&quantize_rows_f16, dim3((unsigned)M), dim3(256), kargs, 0,
+                        stream);
+  }
+  return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
+}
+
 const char* lpgemm_status_string(lpgemm_status status) {
   switch (status) {
     case LPGEMM_SUCCESS: return "success";

@@ -15,6 +15,10 @@ the fixed order A, B, row scales, column scales):
           the error procedure of the forum post on compiler-generated kernels
           (paragraph on hybrid FP16/FP32 accumulation).
 * scales: uniform fp64 in [0.001, 0.01), rounded to fp32.
+* W8A8 activations: standard normal fp64 draws times a per-row magnitude
+          2^u, u uniform in [-4, 4) (rows of very different ranges, as the
+          tokens of a layer's input have), rounded to fp16; then the int8
+          weights and the fp32 weight scales as above.
 
 Layouts: A is M x K row-major; B is stored K-contiguous, i.e. as an N x K
 row-major array (``b_t``); C is M x N row-major.
@@ -38,7 +42,7 @@ LLM_K = 4096
 LLM_N = 14336
 
 # Seed offset per workload family (seed = SEED_BASE + index).
-FAMILY_INDEX = {"i8": 1, "i4": 2, "f16": 3, "llm": 4}
+FAMILY_INDEX = {"i8": 1, "i4": 2, "f16": 3, "llm": 4, "w8a8": 5}
 
 
 def seed_for(family: str, extra: int = 0) -> int:
@@ -120,3 +124,23 @@ def llm_problem(M: int, seed: Optional[int] = None) -> Int8Problem:
     if seed is None:
         seed = seed_for("llm", M)
     return int8_problem(M, LLM_N, LLM_K, seed, scales=True)
+
+
+@dataclass
+class W8A8Problem:
+    x: np.ndarray            # M x K fp16 activations
+    w: np.ndarray            # N x K int8 weights (K-contiguous)
+    w_scale: np.ndarray      # N fp32 weight scales
+
+
+def w8a8_problem(M: int, N: int = LLM_N, K: int = LLM_K, seed: Optional[int] = None) -> W8A8Problem:
+    """fp16 activations for the quantise-then-GEMM projection, with int8
+    weights and per-column fp32 weight scales."""
+    if seed is None:
+        seed = seed_for("w8a8", M)
+    rng = np.random.default_rng(seed)
+    mag = np.exp2(rng.uniform(-4.0, 4.0, size=(M, 1)))
+    x = (rng.standard_normal(size=(M, K)) * mag).astype(np.float16)
+    w = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    ws = rng.uniform(0.001, 0.01, size=N).astype(np.float32)
+    return W8A8Problem(x, w, ws)

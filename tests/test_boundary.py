@@ -20,7 +20,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = b.declared_functions()
     assert set(names) == {"lpgemm_i8", "lpgemm_i4", "lpgemm_f16", "lpgemm_i8_dequant",
-                          "lpgemm_status_string", "lpgemm_version"}
+                          "lpgemm_quantize_rows_f16", "lpgemm_status_string", "lpgemm_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -126,3 +126,19 @@ def test_lpgemm_error_carries_status():
 def test_signature_types(lib):
     assert lib.lpgemm_i8.argtypes[0] is ctypes.c_int64
     assert lib.lpgemm_i8_dequant.restype is ctypes.c_int
+
+
+def test_quantize_validation(lib):
+    q = lib.lpgemm_quantize_rows_f16
+    assert q(-1, 64, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert q(4, -8, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert q(4, 12, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    assert q(4, b.MAX_K_QUANT + 8, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    assert q(0, 64, None, None, None, None) == b.LPGEMM_SUCCESS          # empty: no-op
+    assert q(4, 64, FAKE, FAKE, None, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert q(4, 64, None, FAKE, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert q(4, 64, FAKE, None, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert q(4, 0, None, None, None, None) == b.LPGEMM_ERROR_INVALID_VALUE   # scale still needed
+    assert q(4, 64, MISALIGNED, FAKE, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
+    assert q(4, 64, FAKE, MISALIGNED, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
+    assert q(4, 64, FAKE, FAKE, FAKE + 2, None) == b.LPGEMM_ERROR_MISALIGNED

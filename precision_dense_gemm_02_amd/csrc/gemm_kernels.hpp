@@ -912,13 +912,96 @@ __global__ __launch_bounds__(512) void gemm_pingpong(GemmArgs p) {
 // over k is unchanged, and the two half-waves cover each 128-byte row
 // segment.  The partial sums are combined through LDS in a fixed wave order
 // and the epilogue is applied once per output element.
+// One 128-byte K-block of the skinny kernels: a[mb][q] and b[q] are the
+// 16-byte fragments of step q (lane l: row l % 32 of its 32-row block, bytes
+// 64 (l / 32) + 16 q of the block; A and B use the same assignment, so the
+// sum over k is unchanged).  Packed int4 gives two int8 steps per fragment.
+template <int KIND, int MB>
+__device__ __forceinline__ void skinny_block(typename KindTraits<KIND>::Acc (&acc)[MB],
+                                             const i32x4 (&a)[MB][4], const i32x4 (&b)[4]) {
+  if constexpr (KIND == KIND_I4) {
+    // 64 packed bytes = 8 K-steps of 8 bytes (16 nibbles) each
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t blo, bhi, blo1, bhi1;
+        expand_int4((uint32_t)b[q][2 * half], blo, bhi);
+        expand_int4((uint32_t)b[q][2 * half + 1], blo1, bhi1);
+        const i32x4 bv = {(int)blo, (int)bhi, (int)blo1, (int)bhi1};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          uint32_t alo, ahi, alo1, ahi1;
+          expand_int4((uint32_t)a[mb][q][2 * half], alo, ahi);
+          expand_int4((uint32_t)a[mb][q][2 * half + 1], alo1, ahi1);
+          const i32x4 av = {(int)alo, (int)ahi, (int)alo1, (int)ahi1};
+          acc[mb] = mfma<KIND>(av, bv, acc[mb]);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma<KIND>(a[mb][q], b[q], acc[mb]);
+  }
+}
+
+// Split-K epilogue of the skinny kernels: every wave has written its partial
+// 32*MB x 32 tile to red (rows of kPitch words, wave w's tile starting at
+// word w * kWaveWords); the
+// partials are summed in wave order (a fixed order, so the result does not
+// depend on timing) and the epilogue of the kind is applied once per element.
+template <int KIND, int MT, int NT, int WAVES, int kPitch, int kWaveWords>
+__device__ __forceinline__ void skinny_reduce_store_strided(const GemmArgs& p, const uint32_t* red,
+                                                            int m0, int n0) {
+  for (int idx = threadIdx.x; idx < MT * NT; idx += WAVES * 64) {
+    const int rr = idx / NT, cc = idx % NT;
+    const int row = m0 + rr, col = n0 + cc;
+    if (row >= p.M || col >= p.N) continue;
+    if constexpr (KIND == KIND_F16) {
+      float sum = 0.f;
+      for (int w = 0; w < WAVES; ++w) sum += __builtin_bit_cast(float, red[w * kWaveWords + rr * kPitch + cc]);
+      ((float*)p.C)[(size_t)row * p.N + col] = sum;
+    } else {
+      int32_t sum = 0;
+      for (int w = 0; w < WAVES; ++w) sum += (int32_t)red[w * kWaveWords + rr * kPitch + cc];
+      if constexpr (KIND == KIND_I4) {
+        ((int32_t*)p.C)[(size_t)row * p.N + col] = sum >> 8;   // undo the 16 x 16 scaling
+      } else if constexpr (KIND == KIND_I8_DEQUANT) {
+        float t = (float)sum;
+        t = t * p.row_scale[row];
+        t = t * p.col_scale[col];
+        ((float*)p.C)[(size_t)row * p.N + col] = t;
+      } else {
+        ((int32_t*)p.C)[(size_t)row * p.N + col] = sum;
+      }
+    }
+  }
+}
+
+// Partial sums of one wave -> its slice of red (element e of lane l: row
+// 8*(e/4) + 4*(l/32) + e%4, column l%32 of a 32x32 block).
+template <int KIND, int MB, int kPitch>
+__device__ __forceinline__ void skinny_store_partials(const typename KindTraits<KIND>::Acc (&acc)[MB],
+                                                      uint32_t* mine, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rr = mb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+      // copy the element out first: bit-casting a vector-element lvalue
+      // directly reads the vector's first element
+      const auto v = acc[mb][e];
+      mine[rr * kPitch + r] = __builtin_bit_cast(uint32_t, v);
+    }
+}
+
 template <int KIND, int MB, int WAVES, int CHUNK>
 __global__ __launch_bounds__(WAVES * 64) void gemm_skinny(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
-  constexpr bool I4 = KIND == KIND_I4;
   constexpr int kBlock = 128;
   constexpr int MT = 32 * MB, NT = 32;
-  constexpr int kThreads = WAVES * 64;
   constexpr int kPitch = NT + 1;   // 32-bit words per reduction row
 
   __shared__ __attribute__((aligned(16))) uint32_t red[WAVES * MT * kPitch];
@@ -969,34 +1052,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny(GemmArgs p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0;
 
-  auto compute_block = [&](const i32x4 (&a)[MB][4], const i32x4 (&b)[4]) {
-    if constexpr (I4) {
-      // 64 packed bytes = 8 K-steps of 8 bytes (16 nibbles) each
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          uint32_t blo, bhi, blo1, bhi1;
-          expand_int4((uint32_t)b[q][2 * half], blo, bhi);
-          expand_int4((uint32_t)b[q][2 * half + 1], blo1, bhi1);
-          const i32x4 bv = {(int)blo, (int)bhi, (int)blo1, (int)bhi1};
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            uint32_t alo, ahi, alo1, ahi1;
-            expand_int4((uint32_t)a[mb][q][2 * half], alo, ahi);
-            expand_int4((uint32_t)a[mb][q][2 * half + 1], alo1, ahi1);
-            const i32x4 av = {(int)alo, (int)ahi, (int)alo1, (int)ahi1};
-            acc[mb] = mfma<KIND>(av, bv, acc[mb]);
-          }
-        }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma<KIND>(a[mb][q], b[q], acc[mb]);
-    }
-  };
-
   for (int c = b0; c < b1; c += CHUNK) {
 #pragma unroll
     for (int j = 0; j < CHUNK; ++j) load_block(c + j, fa[j], fb[j]);
@@ -1004,46 +1059,259 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny(GemmArgs p) {
     // otherwise trade memory parallelism for registers)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < CHUNK; ++j) compute_block(fa[j], fb[j]);
+    for (int j = 0; j < CHUNK; ++j) skinny_block<KIND, MB>(acc, fa[j], fb[j]);
   }
 
-  // partial sums -> LDS (element e of lane l: row 8*(e/4) + 4*(l/32) + e%4,
-  // column l%32 of a 32x32 block)
-  uint32_t* mine = red + wave * MT * kPitch;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rr = mb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-      // copy the element out first: bit-casting a vector-element lvalue
-      // directly reads the vector's first element
-      const auto v = acc[mb][e];
-      mine[rr * kPitch + r] = __builtin_bit_cast(uint32_t, v);
-    }
+  skinny_store_partials<KIND, MB, kPitch>(acc, red + wave * MT * kPitch, lane);
   __syncthreads();
-  for (int idx = tid; idx < MT * NT; idx += kThreads) {
-    const int rr = idx / NT, cc = idx % NT;
-    const int row = m0 + rr, col = n0 + cc;
-    if (row >= p.M || col >= p.N) continue;
-    if constexpr (KIND == KIND_F16) {
-      float sum = 0.f;
-      for (int w = 0; w < WAVES; ++w) sum += __builtin_bit_cast(float, red[(w * MT + rr) * kPitch + cc]);
-      ((float*)p.C)[(size_t)row * p.N + col] = sum;
-    } else {
-      int32_t sum = 0;
-      for (int w = 0; w < WAVES; ++w) sum += (int32_t)red[(w * MT + rr) * kPitch + cc];
-      if constexpr (KIND == KIND_I4) {
-        ((int32_t*)p.C)[(size_t)row * p.N + col] = sum >> 8;   // undo the 16 x 16 scaling
-      } else if constexpr (KIND == KIND_I8_DEQUANT) {
-        float t = (float)sum;
-        t = t * p.row_scale[row];
-        t = t * p.col_scale[col];
-        ((float*)p.C)[(size_t)row * p.N + col] = t;
-      } else {
-        ((int32_t*)p.C)[(size_t)row * p.N + col] = sum;
+  skinny_reduce_store_strided<KIND, MT, NT, WAVES, kPitch, MT * kPitch>(p, red, m0, n0);
+}
+
+// Skinny-M kernel with B staged through LDS (M <= 32).  Loading B fragments
+// straight into MFMA registers makes every 16-byte-per-lane load touch 32
+// rows; together with the A loads that request count, not HBM, limits the
+// weight stream.  Here each wave copies R 128-byte K-blocks of the 32 B rows
+// into its own LDS region with direct-to-LDS loads in which lanes 8j .. 8j+7
+// cover one row's whole 128-byte line, then reads the fragments back with
+// ds_read_b128 (the XOR swizzle of the main kernels keeps those reads free of
+// bank conflicts).  A, a few rows shared by every workgroup and mostly L2
+// hits, is still loaded straight into fragments.  Each wave only reads what
+// it loaded itself, so a round needs no barrier: vmcnt(0) covers the copies,
+// and lgkmcnt(0) before the next round's copies makes sure the previous
+// round's fragment reads have completed.  The wave's LDS region then holds
+// its partial sums for the split-K epilogue.
+template <int KIND, int WAVES, int R>
+__global__ __launch_bounds__(WAVES * 64) void gemm_skinny_lds(GemmArgs p) {
+  using Acc = typename KindTraits<KIND>::Acc;
+  constexpr int kBlock = 128;
+  constexpr int MT = 32, NT = 32;
+  constexpr int kPitch = NT + 1;
+  constexpr int kBlockLds = NT * kBlock;      // 4 KiB: one K-block of the 32 B rows
+  constexpr int kWaveLds = R * kBlockLds;
+  static_assert(kWaveLds >= MT * kPitch * 4, "the partial sums reuse the wave's region");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WAVES * kWaveLds];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tm = blockIdx.x / p.tiles_n, tn = blockIdx.x % p.tiles_n;
+  const int m0 = tm * MT, n0 = tn * NT;
+  const int rows_a = min(MT, p.M - m0);
+  const int rows_b = min(NT, p.N - n0);
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.A + (size_t)m0 * p.row_bytes), 0, rows_a * p.row_bytes, kBufferWord3);
+  const i32x4 rsrc_b = make_rsrc(p.B + (size_t)n0 * p.row_bytes, rows_b * p.row_bytes);
+  uint8_t* const my_smem = smem + wave * kWaveLds;
+  const uint32_t my_lds = lds_address(my_smem);
+
+  const int r = lane & 31, h = lane >> 5;
+  const uint32_t row_bytes = (uint32_t)p.row_bytes;
+  const int nblk = p.k_stages;
+  const int b0 = (int)(((long long)nblk * wave) / WAVES);
+  const int b1 = (int)(((long long)nblk * (wave + 1)) / WAVES);
+
+  // Copy slot t of a K-block fills LDS rows 8t .. 8t+7: lane l writes row
+  // 8t + l/8 at chunk position l%8, so it fetches the global chunk whose
+  // swizzled position that is (the XOR swizzle is an involution).
+  uint32_t dma_off[4], dma_col[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = 8 * t + (lane >> 3);
+    const int c = swizzle_chunk(row, lane & 7);
+    dma_off[t] = (uint32_t)row * row_bytes + c * 16;
+    dma_col[t] = c * 16;
+  }
+  const uint32_t a_row = (uint32_t)r * row_bytes;
+  // fragment q of a block: row r, global chunk 4h + q, at its swizzled place
+  int frag_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) frag_off[q] = r * kBlock + (swizzle_chunk(r, 4 * h + q) << 4);
+
+  // one accumulator per K-block of a round: independent MFMA chains, summed
+  // (in a fixed order) before the epilogue
+  Acc acc[R][1];
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][0][e] = 0;
+
+  i32x4 fa[R][1][4], fb[R][4];
+  for (int c = b0; c < b1; c += R) {
+    wait_lgkmcnt0();   // the previous round's fragment reads are done with the region
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int blk = c + j;
+      const uint32_t kbyte = (uint32_t)blk * kBlock;
+      const bool in_range = blk < b1;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool ok = in_range && kbyte + dma_col[t] < row_bytes;
+        lds_dma_16(rsrc_b, my_lds + j * kBlockLds + t * 1024, ok ? dma_off[t] + kbyte : kOutOfRange);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t col = kbyte + (uint32_t)h * 64 + q * 16;
+        const bool ok = in_range && col < row_bytes;
+        fa[j][0][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, ok ? a_row + col : kOutOfRange, 0, 0);
       }
     }
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        fb[j][q] = *(const i32x4*)(my_smem + j * kBlockLds + frag_off[q]);
+#pragma unroll
+    for (int j = 0; j < R; ++j) skinny_block<KIND, 1>(acc[j], fa[j], fb[j]);
   }
+#pragma unroll
+  for (int j = 1; j < R; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[0][0][e] += acc[j][0][e];
+
+  wait_lgkmcnt0();
+  uint32_t* const red = (uint32_t*)smem;
+  skinny_store_partials<KIND, 1, kPitch>(acc[0], (uint32_t*)my_smem, lane);
+  __syncthreads();
+  // wave w's partials start at w * kWaveLds bytes, kWaveLds / 4 words apart
+  skinny_reduce_store_strided<KIND, MT, NT, WAVES, kPitch, kWaveLds / 4>(p, red, m0, n0);
+}
+
+// A 16-byte buffer load into registers issued as inline asm, so that the
+// compiler neither counts it nor places waits for it: the caller waits with
+// wait_vmcnt and then pins the destination with pin_after_wait before any
+// use (the data lands some time after the instruction issues).
+__device__ __forceinline__ void load_16_async(i32x4& dst, const i32x4& rsrc, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(voff), "s"(rsrc) : "memory");
+}
+// Tells the compiler that `x` changes here, so no use of it (or copy of it)
+// is scheduled before the preceding wait.
+__device__ __forceinline__ void pin_after_wait(i32x4& x) { asm volatile("" : "+v"(x)); }
+
+// Skinny-M kernel, B through LDS as in gemm_skinny_lds, with the rounds of
+// each wave double-buffered: the copies and A loads of round i+1 are in
+// flight while round i is read back and contracted, so the weight stream
+// does not stop at every round.  Two LDS regions of R K-blocks per wave; all
+// loads of the loop are inline asm (counted only by the explicit waits):
+// after issuing round i+1, vmcnt(8R) leaves exactly round i+1's 8R loads
+// outstanding, so round i has landed.
+template <int KIND, int WAVES, int R>
+__global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
+  using Acc = typename KindTraits<KIND>::Acc;
+  constexpr int kBlock = 128;
+  constexpr int MT = 32, NT = 32;
+  constexpr int kPitch = NT + 1;
+  constexpr int kBlockLds = NT * kBlock;      // 4 KiB: one K-block of the 32 B rows
+  constexpr int kRoundLds = R * kBlockLds;
+  constexpr int kWaveLds = 2 * kRoundLds;
+  constexpr int kLoadsPerRound = 8 * R;       // 4 copies + 4 A fragments per block
+  static_assert(kWaveLds >= MT * kPitch * 4, "the partial sums reuse the wave's region");
+  // two rounds can be outstanding at once; the vector-memory counter holds
+  // at most 63, and a wait on a counter that has overflowed passes too early
+  static_assert(2 * kLoadsPerRound <= 63, "two rounds of loads must fit the vmcnt counter");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WAVES * kWaveLds];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tm = blockIdx.x / p.tiles_n, tn = blockIdx.x % p.tiles_n;
+  const int m0 = tm * MT, n0 = tn * NT;
+  const int rows_a = min(MT, p.M - m0);
+  const int rows_b = min(NT, p.N - n0);
+  const i32x4 rsrc_a = make_rsrc(p.A + (size_t)m0 * p.row_bytes, rows_a * p.row_bytes);
+  const i32x4 rsrc_b = make_rsrc(p.B + (size_t)n0 * p.row_bytes, rows_b * p.row_bytes);
+  uint8_t* const my_smem = smem + wave * kWaveLds;
+  const uint32_t my_lds = lds_address(my_smem);
+
+  const int r = lane & 31, h = lane >> 5;
+  const uint32_t row_bytes = (uint32_t)p.row_bytes;
+  const int nblk = p.k_stages;
+  const int b0 = (int)(((long long)nblk * wave) / WAVES);
+  const int b1 = (int)(((long long)nblk * (wave + 1)) / WAVES);
+  const int rounds = (b1 - b0 + R - 1) / R;
+
+  uint32_t dma_off[4], dma_col[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = 8 * t + (lane >> 3);
+    const int c = swizzle_chunk(row, lane & 7);
+    dma_off[t] = (uint32_t)row * row_bytes + c * 16;
+    dma_col[t] = c * 16;
+  }
+  const uint32_t a_row = (uint32_t)r * row_bytes;
+  int frag_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) frag_off[q] = r * kBlock + (swizzle_chunk(r, 4 * h + q) << 4);
+
+  Acc acc[R][1];
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][0][e] = 0;
+
+  i32x4 fa[2][R][1][4];
+
+  // round i: K-blocks b0 + R i .. + R - 1 into region `buf`
+  auto issue = [&](int i, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int blk = b0 + R * i + j;
+      const uint32_t kbyte = (uint32_t)blk * kBlock;
+      const bool in_range = blk < b1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t col = kbyte + (uint32_t)h * 64 + q * 16;
+        const bool ok = in_range && col < row_bytes;
+        load_16_async(fa[buf][j][0][q], rsrc_a, ok ? a_row + col : kOutOfRange);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool ok = in_range && kbyte + dma_col[t] < row_bytes;
+        lds_dma_16(rsrc_b, my_lds + buf * kRoundLds + j * kBlockLds + t * 1024,
+                   ok ? dma_off[t] + kbyte : kOutOfRange);
+      }
+    }
+  };
+  // contract round i from region `buf`, first starting round i + 1 (if any)
+  // in the other region
+  auto step = [&](int i, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    if (i + 1 < rounds) {
+      wait_lgkmcnt0();   // the other region's fragment reads (round i - 1) are complete
+      issue(i + 1, std::integral_constant<int, 1 - buf>());
+      wait_vmcnt<kLoadsPerRound>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    i32x4 fb[R][4];
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        pin_after_wait(fa[buf][j][0][q]);
+        fb[j][q] = *(const i32x4*)(my_smem + buf * kRoundLds + j * kBlockLds + frag_off[q]);
+      }
+#pragma unroll
+    for (int j = 0; j < R; ++j) skinny_block<KIND, 1>(acc[j], fa[buf][j], fb[j]);
+  };
+
+  if (rounds > 0) issue(0, std::integral_constant<int, 0>());
+  for (int i = 0; i < rounds; i += 2) {
+    step(i, std::integral_constant<int, 0>());
+    if (i + 1 < rounds) step(i + 1, std::integral_constant<int, 1>());
+  }
+#pragma unroll
+  for (int j = 1; j < R; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[0][0][e] += acc[j][0][e];
+
+  wait_lgkmcnt0();
+  skinny_store_partials<KIND, 1, kPitch>(acc[0], (uint32_t*)my_smem, lane);
+  __syncthreads();
+  skinny_reduce_store_strided<KIND, MT, NT, WAVES, kPitch, kWaveLds / 4>(p, (const uint32_t*)smem, m0, n0);
 }
 
 // ---------------------------------------------------------------------------

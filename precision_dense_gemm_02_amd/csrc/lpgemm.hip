@@ -96,7 +96,14 @@ enum KernelCfg {
   CFG_SKINNY_32 = 8,     // 32 x 32 tiles, 8 waves split K, 4 K-blocks per load round
   CFG_SKINNY_64 = 9,     // 64 x 32 tiles, 8 waves split K, 2 K-blocks per load round
   CFG_SKINNY_32_W16 = 10,  // 32 x 32 tiles, 16 waves split K, 2 K-blocks per load round
-  CFG_COUNT = 11
+  CFG_SKINNY_LDS_R2 = 11,  // 32 x 32 tiles, 8 waves split K, B through LDS, 2 K-blocks per round
+  CFG_SKINNY_LDS_R4 = 12,  // 32 x 32 tiles, 8 waves split K, B through LDS, 4 K-blocks per round
+  CFG_SKINNY_LDS_W4 = 13,  // 32 x 32 tiles, 4 waves split K, B through LDS, 4 K-blocks per round
+  CFG_SKINNY_PIPE_W4R2 = 14,  // as 13, double-buffered rounds of 2 K-blocks
+  CFG_SKINNY_PIPE_W8R1 = 15,  // 8 waves, double-buffered rounds of 1 K-block
+  CFG_SKINNY_PIPE_W4R3 = 16,  // 4 waves, double-buffered rounds of 3 K-blocks
+  CFG_SKINNY_PIPE_W8R2 = 17,  // 8 waves, double-buffered rounds of 2 K-blocks
+  CFG_COUNT = 18
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -106,7 +113,7 @@ int stage_row_bytes(KernelCfg c) {
                                                                                                  : 128;
 }
 bool expands_int4_in_lds(KernelCfg c) { return c >= CFG_V1_256x256 && c <= CFG_V1_64x64; }
-bool is_skinny(KernelCfg c) { return c >= CFG_SKINNY_32 && c <= CFG_SKINNY_32_W16; }
+bool is_skinny(KernelCfg c) { return c >= CFG_SKINNY_32 && c <= CFG_SKINNY_PIPE_W8R2; }
 
 int tiles(int64_t x, int t) { return (int)((x + t - 1) / t); }
 
@@ -125,7 +132,7 @@ KernelCfg choose_config(int64_t M, int64_t N, int cu_count) {
   const int f = forced_config();
   if (f >= 0) return (KernelCfg)f;
   // few rows against many columns: stream B with split-K workgroups
-  if (M <= 32) return CFG_SKINNY_32;
+  if (M <= 32) return CFG_SKINNY_PIPE_W4R2;
   if (M <= 64) return CFG_SKINNY_64;
   if (M <= 128) return CFG_128_S4_R64;
   const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
@@ -195,6 +202,20 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<64, 32>((const void*)&gemm_skinny<KIND, 2, 8, 2>, args, 512, stream);
     case CFG_SKINNY_32_W16:
       return launch<32, 32>((const void*)&gemm_skinny<KIND, 1, 16, 2>, args, 1024, stream);
+    case CFG_SKINNY_LDS_R2:
+      return launch<32, 32>((const void*)&gemm_skinny_lds<KIND, 8, 2>, args, 512, stream);
+    case CFG_SKINNY_LDS_R4:
+      return launch<32, 32>((const void*)&gemm_skinny_lds<KIND, 8, 4>, args, 512, stream);
+    case CFG_SKINNY_LDS_W4:
+      return launch<32, 32>((const void*)&gemm_skinny_lds<KIND, 4, 4>, args, 256, stream);
+    case CFG_SKINNY_PIPE_W4R2:
+      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 4, 2>, args, 256, stream);
+    case CFG_SKINNY_PIPE_W8R1:
+      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 8, 1>, args, 512, stream);
+    case CFG_SKINNY_PIPE_W4R3:
+      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 4, 3>, args, 256, stream);
+    case CFG_SKINNY_PIPE_W8R2:
+      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 8, 2>, args, 512, stream);
     default:
       return launch<64, 64>((const void*)&gemm_tiled<KIND, 64, 64, 2, 2>, args, 256, stream);
   }

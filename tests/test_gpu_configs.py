@@ -13,7 +13,7 @@ from precision_dense_gemm_02_amd import inputs  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = range(11)
+CONFIGS = range(18)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -93,3 +93,23 @@ def test_int4_range_limit(forced):
     torch.cuda.synchronize()
     ref = np.where(np.arange(N)[None, :] % 2 == 1, -56 * K, 64 * K).astype(np.int32)
     np.testing.assert_array_equal(out.cpu().numpy(), np.broadcast_to(ref, (M, N)))
+
+
+@pytest.mark.parametrize("forced", CONFIGS, indirect=True)
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_skinny_long_k(forced, M):
+    # several load rounds per wave of the split-K kernels, with a ragged last
+    # K-block and N off the 32-column tile grid
+    N = 100
+    for K in (4112, 1040):
+        print("[case] cfg", forced, "i8 long K", M, N, K, flush=True)
+        p = inputs.int8_problem(M, N, K, seed=M + K + forced, scales=True)
+        out = lp.gemm_i8_dequant(_dev(p.a), _dev(p.b_t), _dev(p.row_scale), _dev(p.col_scale))
+        torch.cuda.synchronize()
+        ref = oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale)
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+        f = inputs.f16_problem(M, N, K, seed=M + K + forced)
+        out = lp.gemm_f16(_dev(f.a), _dev(f.b_t))
+        torch.cuda.synchronize()
+        ref, den = oracle.gemm_f16(f.a, f.b_t)
+        assert oracle.f16_rel_error(out.cpu().numpy(), ref, den)["max_rel"] <= 1e-3

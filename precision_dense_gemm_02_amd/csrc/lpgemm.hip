@@ -103,14 +103,20 @@ enum KernelCfg {
   CFG_SKINNY_PIPE_W8R1 = 15,  // 8 waves, double-buffered rounds of 1 K-block
   CFG_SKINNY_PIPE_W4R3 = 16,  // 4 waves, double-buffered rounds of 3 K-blocks
   CFG_SKINNY_PIPE_W8R2 = 17,  // 8 waves, double-buffered rounds of 2 K-blocks
-  CFG_COUNT = 18
+  CFG_128x64_S4_R64 = 18,     // 4 waves, 128 x 64, 4 stages of 64-byte rows
+  CFG_256x128_S4_R64 = 19,    // 4 waves, 256 x 128, 4 stages of 64-byte rows
+  CFG_128x64_S6_R128 = 20,    // 4 waves, 128 x 64, 6 stages of 128-byte rows
+  CFG_128x64_S8_R64 = 21,     // 4 waves, 128 x 64, 8 stages of 64-byte rows
+  CFG_COUNT = 22
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
 // kernels expand int4 to int8 on the way into LDS, 128 values per stage).
 int stage_row_bytes(KernelCfg c) {
-  return (c == CFG_256_S4_R64 || c == CFG_256_S3_R64 || c == CFG_128_S4_R64 || c == CFG_PP_R64) ? 64
-                                                                                                 : 128;
+  return (c == CFG_256_S4_R64 || c == CFG_256_S3_R64 || c == CFG_128_S4_R64 || c == CFG_PP_R64 ||
+          c == CFG_128x64_S4_R64 || c == CFG_256x128_S4_R64 || c == CFG_128x64_S8_R64)
+             ? 64
+             : 128;
 }
 bool expands_int4_in_lds(KernelCfg c) { return c >= CFG_V1_256x256 && c <= CFG_V1_64x64; }
 bool is_skinny(KernelCfg c) { return c >= CFG_SKINNY_32 && c <= CFG_SKINNY_PIPE_W8R2; }
@@ -134,7 +140,9 @@ KernelCfg choose_config(int64_t M, int64_t N, int cu_count) {
   // few rows against many columns: stream B with split-K workgroups
   if (M <= 32) return CFG_SKINNY_PIPE_W4R2;
   if (M <= 64) return CFG_SKINNY_64;
-  if (M <= 128) return CFG_128_S4_R64;
+  // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128, and
+  // six 128-byte stages keep more of the streamed B operand in flight
+  if (M <= 128) return CFG_128x64_S6_R128;
   const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
   if (big >= cu_count) return CFG_256_S2_R128;
   const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
@@ -216,6 +224,14 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 4, 3>, args, 256, stream);
     case CFG_SKINNY_PIPE_W8R2:
       return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 8, 2>, args, 512, stream);
+    case CFG_128x64_S4_R64:
+      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 4, 64>, args, 256, stream);
+    case CFG_256x128_S4_R64:
+      return launch<256, 128>((const void*)&gemm_v3<KIND, 256, 128, 4, 64>, args, 256, stream);
+    case CFG_128x64_S6_R128:
+      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128>, args, 256, stream);
+    case CFG_128x64_S8_R64:
+      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 8, 64>, args, 256, stream);
     default:
       return launch<64, 64>((const void*)&gemm_tiled<KIND, 64, 64, 2, 2>, args, 256, stream);
   }

@@ -38,10 +38,12 @@ if ROOT not in sys.path:
 METRIC = "INT8/INT4 TOPS and FP16 TFLOPS at N=8192 on 1 MI355X; % of MFMA peak"
 # Dense MFMA peaks of the MI355X (256 CUs, 2.4 GHz): int8 8192 ops and fp16
 # 4096 flops per CU per clock.  INT4 runs on the int8 MFMA.
-PEAK_TOPS = {"i8": 5033.2, "i4": 5033.2, "dq": 5033.2, "w8": 5033.2, "f16": 2516.6}
+PEAK_TOPS = {"i8": 5033.2, "i4": 5033.2, "dq": 5033.2, "w8": 5033.2, "f16": 2516.6,
+             "i4e": 5033.2, "i4g": 5033.2}
 HBM_PEAK_GBS = 8000.0
-UNIT = {"i8": "TOPS", "i4": "TOPS", "dq": "TOPS", "w8": "TOPS", "f16": "TFLOPS"}
-DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "w8": "i8", "f16": "f16"}
+UNIT = {"i8": "TOPS", "i4": "TOPS", "dq": "TOPS", "w8": "TOPS", "f16": "TFLOPS", "i4e": "TOPS",
+        "i4g": "TOPS"}
+DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "w8": "i8", "f16": "f16", "i4e": "i4", "i4g": "i4"}
 KERNEL_SOURCES = ["precision_dense_gemm_02_amd/csrc/gemm_kernels.hpp",
                   "precision_dense_gemm_02_amd/csrc/lpgemm.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -64,7 +66,7 @@ def parse_workload(name: str):
     if kind == "w8a8":
         from precision_dense_gemm_02_amd import inputs
         return "w8", size, inputs.LLM_N, inputs.LLM_K
-    if kind not in ("i8", "i4", "f16"):
+    if kind not in ("i8", "i4", "f16", "i4e", "i4g"):
         raise SystemExit(f"unknown workload {name}")
     return kind, size, size, size
 
@@ -105,6 +107,29 @@ class Workload:
             out = torch.empty((M, N), dtype=torch.int32, device=dev)
             self.launch = lambda i: lp.gemm_i4(a, b, K, out=out)
             self.in_bytes = (M * K + N * K) // 2
+            self.out_bytes = 4 * M * N
+        elif kind in ("i4e", "i4g"):
+            # int4 through the FP6 E3M2 matrix cores.  i4e: both operands are
+            # re-encoded inside the step (three launches); i4g: the GEMM alone
+            # on operands re-encoded beforehand (weights converted once)
+            self.seed = inputs.seed_for("i4", M)
+            p = inputs.int4_problem(M, N, K, self.seed)
+            self.host = p
+            a, b = to(p.a_packed), to(p.b_packed)
+            a6 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            b6 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+            out = torch.empty((M, N), dtype=torch.int32, device=dev)
+            if kind == "i4e":
+                def step(i):
+                    lp.i4_to_e3m2(a, out=a6)
+                    lp.i4_to_e3m2(b, out=b6)
+                    lp.gemm_i4_e3m2(a6, b6, out=out)
+                self.launch = step
+            else:
+                lp.i4_to_e3m2(a, out=a6)
+                lp.i4_to_e3m2(b, out=b6)
+                self.launch = lambda i: lp.gemm_i4_e3m2(a6, b6, out=out)
+            self.in_bytes = (M * K + N * K) // 2 if kind == "i4e" else M * K + N * K
             self.out_bytes = 4 * M * N
         elif kind == "f16":
             self.seed = inputs.seed_for("f16", M)
@@ -160,7 +185,7 @@ class Workload:
         p = self.host
         if self.kind == "i8":
             ok = np.array_equal(got, oracle.gemm_i8(p.a, p.b_t, rows=rows))
-        elif self.kind == "i4":
+        elif self.kind in ("i4", "i4e", "i4g"):
             ok = np.array_equal(got, oracle.gemm_i4(p.a_packed, p.b_packed, self.K, rows=rows))
         elif self.kind == "f16":
             ref, den = oracle.gemm_f16(p.a, p.b_t, rows=rows)
@@ -265,7 +290,7 @@ def cpu_baseline(w: Workload, seconds: float) -> dict:
         t0 = time.perf_counter()
         if w.kind == "i8":
             oracle.gemm_i8(p.a, p.b_t, rows=rows)
-        elif w.kind == "i4":
+        elif w.kind in ("i4", "i4e", "i4g"):
             oracle.gemm_i4(p.a_packed, p.b_packed, w.K, rows=rows)
         elif w.kind == "f16":
             oracle.gemm_f16(p.a, p.b_t, rows=rows)
@@ -305,6 +330,12 @@ def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
     if w.kind == "w8":
         rec["note"] = ("one step is two launches (per-row quantise, then the dequantising "
                        "GEMM); the kernel time and roofline cover both")
+    elif w.kind == "i4e":
+        rec["note"] = ("int4 through the FP6 E3M2 MFMA: one step is three launches (re-encode "
+                       "A, re-encode B, GEMM); the kernel time and roofline cover all three")
+    elif w.kind == "i4g":
+        rec["note"] = ("int4 through the FP6 E3M2 MFMA, GEMM launch only: operands re-encoded "
+                       "before timing (weights converted once)")
     return w, rec
 
 

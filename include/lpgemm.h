@@ -94,6 +94,28 @@ lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, const 
 lpgemm_status lpgemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A_packed,
                         const uint8_t *B_packed, int32_t *C, hipStream_t stream);
 
+/* INT4 through FP6 E3M2 matrix cores, step 1 of 2: re-encode packed int4
+ * rows (the layout of lpgemm_i4: two values per byte along k, low nibble =
+ * even k, two's complement) as E3M2 operand rows.  Every value in [-8, 7] is
+ * exact in E3M2; gfx950 multiplies FP6 operands at about twice its int8 rate
+ * (a route to the PTX-vs-WMMA summary page's native 4-bit tensor-core path,
+ * which this chip lacks for integers).  src_packed: rows x K/2 bytes;
+ * dst: rows x K bytes, each group of 32 values becoming 24 bytes of six-bit
+ * codes followed by 8 zero bytes (the codes in an order private to the
+ * library; dst is meant only for lpgemm_i4_e3m2).  K must be a multiple of
+ * 32 and at most LPGEMM_MAX_K_INT; both pointers 16-byte aligned.  rows = 0
+ * or K = 0 is a no-op.  Weights that do not change need converting once. */
+lpgemm_status lpgemm_i4_to_e3m2(int64_t rows, int64_t K, const uint8_t *src_packed, uint8_t *dst,
+                                hipStream_t stream);
+
+/* INT4 through FP6 E3M2, step 2 of 2: C = A . B exactly in int32 for int4
+ * operands that lpgemm_i4_to_e3m2 has re-encoded (A_e3m2: M x K bytes,
+ * B_e3m2: N x K bytes).  Products are at most 64 and the fp32 sums are
+ * integers below 2^24 for K <= LPGEMM_MAX_K_INT, so the result equals
+ * lpgemm_i4's bit for bit.  Shapes, alignment and errors as for lpgemm_i4. */
+lpgemm_status lpgemm_i4_e3m2(int64_t M, int64_t N, int64_t K, const uint8_t *A_e3m2,
+                             const uint8_t *B_e3m2, int32_t *C, hipStream_t stream);
+
 /* FP16: C[i][j] = sum_k A[i][k] * B[k][j] with binary16 operands, products
  * and sums in binary32 (the summation order is unspecified).  A: M x K,
  * B: N x K (K-contiguous), C: M x N fp32.  The pointers have the bit layout of

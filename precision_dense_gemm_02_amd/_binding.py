@@ -61,6 +61,10 @@ def load_library():
         lib.lpgemm_i8_dequant.restype = ctypes.c_int
         lib.lpgemm_quantize_rows_f16.argtypes = [_i64, _i64, _p, _p, _p, _p]
         lib.lpgemm_quantize_rows_f16.restype = ctypes.c_int
+        lib.lpgemm_i4_to_e3m2.argtypes = [_i64, _i64, _p, _p, _p]
+        lib.lpgemm_i4_to_e3m2.restype = ctypes.c_int
+        lib.lpgemm_i4_e3m2.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p]
+        lib.lpgemm_i4_e3m2.restype = ctypes.c_int
         lib.lpgemm_status_string.argtypes = [ctypes.c_int]
         lib.lpgemm_status_string.restype = ctypes.c_char_p
         lib.lpgemm_version.argtypes = []
@@ -241,3 +245,42 @@ def w8a8_linear(x, w, w_scale, out=None):
     function allocates) and lpgemm_i8_dequant."""
     q, s = quantize_rows_f16(x)
     return gemm_i8_dequant(q, w, s, w_scale, out=out)
+
+
+def i4_to_e3m2(packed, out=None):
+    """Re-encode packed int4 rows (rows x K/2 uint8, low nibble = even k) as
+    the FP6 E3M2 operand rows that gemm_i4_e3m2 takes (rows x K uint8)."""
+    torch = _torch()
+    _operand(packed, torch.uint8, "packed")
+    rows, half = packed.shape
+    K = 2 * half
+    out = _output(out, (rows, K), torch.uint8, packed.device)
+    with torch.cuda.device(packed.device):
+        _check(load_library().lpgemm_i4_to_e3m2(rows, K, packed.data_ptr(), out.data_ptr(),
+                                                _stream_handle(packed.device)), "lpgemm_i4_to_e3m2")
+    return out
+
+
+def gemm_i4_e3m2(a_e3m2, b_e3m2, out=None):
+    """int32 C = A . B for int4 operands re-encoded by i4_to_e3m2 (M x K and
+    N x K uint8); equal to gemm_i4 on the packed operands."""
+    torch = _torch()
+    _operand(a_e3m2, torch.uint8, "a_e3m2")
+    _operand(b_e3m2, torch.uint8, "b_e3m2")
+    if a_e3m2.shape[1] != b_e3m2.shape[1]:
+        raise ValueError("K mismatch")
+    dev = _same_device(a_e3m2, b_e3m2)
+    M, K = a_e3m2.shape
+    N = b_e3m2.shape[0]
+    out = _output(out, (M, N), torch.int32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_i4_e3m2(M, N, K, a_e3m2.data_ptr(), b_e3m2.data_ptr(),
+                                             out.data_ptr(), _stream_handle(dev)), "lpgemm_i4_e3m2")
+    return out
+
+
+def gemm_i4_via_e3m2(a_packed, b_packed, out=None):
+    """gemm_i4 through the FP6 matrix cores: both operands are re-encoded
+    (into buffers this function allocates), then multiplied; three library
+    calls on the current stream."""
+    return gemm_i4_e3m2(i4_to_e3m2(a_packed), i4_to_e3m2(b_packed), out=out)

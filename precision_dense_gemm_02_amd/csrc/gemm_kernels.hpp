@@ -34,7 +34,7 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-enum Kind : int { KIND_I8 = 0, KIND_I4 = 1, KIND_F16 = 2, KIND_I8_DEQUANT = 3 };
+enum Kind : int { KIND_I8 = 0, KIND_I4 = 1, KIND_F16 = 2, KIND_I8_DEQUANT = 3, KIND_I4_E3M2 = 4 };
 
 // LDS bytes of one operand row per K-stage, and 16-byte chunks per such row.
 constexpr int kStageRowBytes = 128;
@@ -126,6 +126,23 @@ struct KindTraits<KIND_F16> {
   static constexpr int global_chunks = kChunksPerRow;
   using Acc = f32x16;
 };
+// int4 values re-encoded as FP6 E3M2, one byte per value (see
+// pack_i4_e3m2): products and their sums are integers below 2^24, exact in
+// the fp32 accumulator
+template <>
+struct KindTraits<KIND_I4_E3M2> {
+  static constexpr int global_chunks = kChunksPerRow;
+  using Acc = f32x16;
+};
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32 x 32 x 64 MFMA on FP6 E3M2 operands (format 3 of the f8f6f4 family),
+// both block scales 2^0 (E8M0 127).  Each lane supplies 32 values of K in
+// the low six dwords.
+__device__ __forceinline__ f32x16 mfma_e3m2(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 3, 3, 0, 127, 0, 127);
+}
 
 template <int KIND>
 __device__ __forceinline__ typename KindTraits<KIND>::Acc mfma(const i32x4& a, const i32x4& b,
@@ -447,8 +464,14 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
   constexpr bool I4 = KIND == KIND_I4;
-  constexpr int kStepBytes = I4 ? 16 : 32;           // row bytes one MFMA K-step consumes
+  constexpr bool E3M2 = KIND == KIND_I4_E3M2;
+  // row bytes one MFMA K-step consumes: 32 packed int4 (16 B) expand to one
+  // int8 step; an E3M2 step is 64 values in two 32-byte groups
+  constexpr int kStepBytes = I4 ? 16 : (E3M2 ? 64 : 32);
   constexpr int KSTEPS = ROWB / kStepBytes;
+  // the two fragment buffers alternate per K-step and the next stage's first
+  // step reads into buffer 0 again, so a stage needs an even number of steps
+  static_assert(KSTEPS % 2 == 0, "K-steps per stage must be even");
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM % 2 == 0 && TN >= 1 && BM % 128 == 0 && BN % 64 == 0, "tile");
@@ -514,24 +537,46 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   const int b_row_base = (BM + wn * WTN) * ROWB;
   auto frag_off = [&](int kk) -> int {
     if constexpr (I4) return Layout::off(fr, kk) + fh * 8;       // 8 packed bytes
+    else if constexpr (E3M2) return Layout::off(fr, 4 * kk + 2 * fh);   // group, first chunk
     else return Layout::off(fr, 2 * kk + fh);                     // 16 bytes
   };
+  // E3M2: the group's second chunk holds codes in its first 8 bytes (the
+  // other 8 are padding and are not read)
+  auto frag_off2 = [&](int kk) -> int { return Layout::off(fr, 4 * kk + 2 * fh + 1); };
 
-  using Raw = typename std::conditional<I4, i32x2_t, i32x4>::type;
+  // E3M2 fragments are read straight into the eight-dword MFMA operand (of
+  // which the FP6 format uses the low six)
+  using Raw = typename std::conditional<I4, i32x2_t, typename std::conditional<E3M2, i32x8, i32x4>::type>::type;
+  using Op = typename std::conditional<E3M2, i32x8, i32x4>::type;
+  auto e3m2_frag = [](const uint8_t* p0, const uint8_t* p1) -> i32x8 {
+    const i32x4 lo = *(const i32x4*)p0;
+    const i32x2_t hi = *(const i32x2_t*)p1;
+    return __builtin_shufflevector(lo, __builtin_shufflevector(hi, hi, 0, 1, -1, -1), 0, 1, 2, 3, 4, 5, 6, 7);
+  };
   Raw fa[2][TM], fb[2][TN];
 
   auto read_frags = [&](int s, int kk, int dst) {
     const uint8_t* base = smem + (s % STAGES) * kStage;
     const int off = frag_off(kk);
+    if constexpr (E3M2) {
+      const int off2 = frag_off2(kk);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      fa[dst][i] = *(const Raw*)(base + a_row_base + i * 32 * ROWB + off);
+      for (int i = 0; i < TM; ++i)
+        fa[dst][i] = e3m2_frag(base + a_row_base + i * 32 * ROWB + off, base + a_row_base + i * 32 * ROWB + off2);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      fb[dst][j] = *(const Raw*)(base + b_row_base + j * 32 * ROWB + off);
+      for (int j = 0; j < TN; ++j)
+        fb[dst][j] = e3m2_frag(base + b_row_base + j * 32 * ROWB + off, base + b_row_base + j * 32 * ROWB + off2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[dst][i] = *(const Raw*)(base + a_row_base + i * 32 * ROWB + off);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[dst][j] = *(const Raw*)(base + b_row_base + j * 32 * ROWB + off);
+    }
   };
 
-  auto operand = [&](const Raw& r) -> i32x4 {
+  auto operand = [&](const Raw& r) -> Op {
     if constexpr (I4) {
       uint32_t lo0, hi0, lo1, hi1;
       expand_int4((uint32_t)r.x, lo0, hi0);
@@ -551,7 +596,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
   auto compute = [&](int src, int first, int last) {
-    i32x4 a[TM], b[TN];
+    Op a[TM], b[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) a[i] = operand(fa[src][i]);
 #pragma unroll
@@ -560,12 +605,13 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     for (int x = 0; x < TM * TN; ++x) {
       if (x < first || x >= last) continue;
       const int i = x / TN, j = x % TN;
-      acc[i][j] = mfma<KIND>(a[i], b[j], acc[i][j]);
+      if constexpr (E3M2) acc[i][j] = mfma_e3m2(a[i], b[j], acc[i][j]);
+      else acc[i][j] = mfma<KIND>(a[i], b[j], acc[i][j]);
     }
   };
 
   constexpr int kMfma = TM * TN;
-  constexpr int kReads = TM + TN;
+  constexpr int kReads = (E3M2 ? 2 : 1) * (TM + TN);   // DS read instructions per K-step
   // loads of one stage are spread over K-steps 0 .. KSTEPS-2 (or step 0)
   constexpr int kLoadSteps = KSTEPS > 1 ? KSTEPS - 1 : 1;
   constexpr int kLoadsPerStep = (kSlots + kLoadSteps - 1) / kLoadSteps;
@@ -629,6 +675,8 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   auto value = [&](int i, int j, int e, int row, int col) -> uint32_t {
     if constexpr (KIND == KIND_F16) {
       return __builtin_bit_cast(uint32_t, (float)acc[i][j][e]);
+    } else if constexpr (E3M2) {
+      return (uint32_t)(int32_t)acc[i][j][e];   // an integer below 2^24: exact
     } else if constexpr (KIND == KIND_I4) {
       return (uint32_t)(acc[i][j][e] >> 8);   // undo the 16 x 16 scaling
     } else if constexpr (KIND == KIND_I8_DEQUANT) {
@@ -1312,6 +1360,59 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   skinny_store_partials<KIND, 1, kPitch>(acc[0], (uint32_t*)my_smem, lane);
   __syncthreads();
   skinny_reduce_store_strided<KIND, MT, NT, WAVES, kPitch, kWaveLds / 4>(p, (const uint32_t*)smem, m0, n0);
+}
+
+// ---------------------------------------------------------------------------
+// Packed int4 -> FP6 E3M2 operand rows for the E3M2 MFMA.
+//
+// Every int4 value v in [-8, 7] is exact in E3M2 (1 sign, 3 exponent bits
+// with bias 3, 2 mantissa bits): 1 = 1.0 x 2^0, 3 = 1.5 x 2^1, 5 = 1.25 x 2^2,
+// 7 = 1.75 x 2^2, 8 = 1.0 x 2^3, and so on.  A group of 32 values of one row
+// (16 packed bytes) becomes 32 bytes: 32 six-bit codes packed little-endian
+// into 24 bytes, then 8 zero bytes, so a row of K values takes K bytes and
+// a group is two 16-byte chunks (the layout the LDS swizzle works in).
+//
+// Within a group the codes are stored in the order k = 0, 2, 4, 6, 1, 3, 5,
+// 7, 8, 10, ...: even and odd nibbles of each packed dword are looked up
+// separately.  The MFMA pairs slot i of A with slot i of B, and both
+// operands use this order, so the sum over k is unchanged.
+//
+// Code lookup, four nibbles at a time: v_perm_b32 picks bytes from an
+// eight-byte table, one table for nibbles 0..7 (v = 0..7) and one for
+// 8..15 (v = -8..-1); the nibble's bit 3 selects between them.
+__device__ __forceinline__ uint32_t e3m2_codes(uint32_t nib4) {
+  // table bytes: codes of v = 0..7 and of v = -8..-1
+  constexpr uint32_t kPosLo = 0x12100C00u, kPosHi = 0x17161514u;
+  constexpr uint32_t kNegLo = 0x35363738u, kNegHi = 0x2C303234u;
+  const uint32_t idx = nib4 & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(kPosHi, kPosLo, idx);
+  const uint32_t neg = __builtin_amdgcn_perm(kNegHi, kNegLo, idx);
+  const uint32_t mask = ((nib4 >> 3) & 0x01010101u) * 0xFFu;   // 0xFF where v < 0
+  return (neg & mask) | (pos & ~mask);
+}
+// four six-bit codes (one per byte) -> 24 contiguous bits
+__device__ __forceinline__ uint32_t pack4_6bit(uint32_t c) {
+  return (c & 0x3Fu) | ((c >> 2) & 0xFC0u) | ((c >> 4) & 0x3F000u) | ((c >> 6) & 0xFC0000u);
+}
+
+__global__ __launch_bounds__(256) void pack_i4_e3m2(const uint8_t* __restrict__ src,
+                                                    uint8_t* __restrict__ dst, int64_t groups) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= groups) return;
+  const i32x4 x = ((const i32x4*)src)[g];
+  uint32_t q[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t w = (uint32_t)x[d];
+    q[2 * d] = pack4_6bit(e3m2_codes(w & 0x0F0F0F0Fu));          // k = 8d, 8d+2, 8d+4, 8d+6
+    q[2 * d + 1] = pack4_6bit(e3m2_codes((w >> 4) & 0x0F0F0F0Fu)); // k = 8d+1, ..., 8d+7
+  }
+  // eight 24-bit pieces -> six dwords
+  const i32x4 lo = {(int)(q[0] | (q[1] << 24)), (int)((q[1] >> 8) | (q[2] << 16)),
+                    (int)((q[2] >> 16) | (q[3] << 8)), (int)(q[4] | (q[5] << 24))};
+  const i32x4 hi = {(int)((q[5] >> 8) | (q[6] << 16)), (int)((q[6] >> 16) | (q[7] << 8)), 0, 0};
+  ((i32x4*)dst)[2 * g] = lo;
+  ((i32x4*)dst)[2 * g + 1] = hi;
 }
 
 // ---------------------------------------------------------------------------

@@ -62,6 +62,7 @@ lpgemm_status validate(Kind kind, int64_t M, int64_t N, int64_t K, const void* A
       if (K % 16 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
       break;
     case KIND_I4:
+    case KIND_I4_E3M2:
       if (K % 32 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
       break;
     case KIND_F16:
@@ -107,7 +108,8 @@ enum KernelCfg {
   CFG_256x128_S4_R64 = 19,    // 4 waves, 256 x 128, 4 stages of 64-byte rows
   CFG_128x64_S6_R128 = 20,    // 4 waves, 128 x 64, 6 stages of 128-byte rows
   CFG_128x64_S8_R64 = 21,     // 4 waves, 128 x 64, 8 stages of 64-byte rows
-  CFG_COUNT = 22
+  CFG_128_S4_R128 = 22,       // 4 waves, 128 x 128, 4 stages of 128-byte rows
+  CFG_COUNT = 23
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -132,6 +134,21 @@ int forced_config() {
   char* end = nullptr;
   const long v = std::strtol(e, &end, 10);
   return (end && *end == 0 && v >= 0 && v < CFG_COUNT) ? (int)v : -1;
+}
+
+// The E3M2 kind runs only on the LDS-pipelined kernels with 128-byte stage
+// rows (two 64-value MFMA steps per stage).
+bool supports_e3m2(int c) {
+  return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128;
+}
+
+KernelCfg choose_config_e3m2(int64_t M, int64_t N, int cu_count) {
+  const int f = forced_config();
+  if (f >= 0 && supports_e3m2(f)) return (KernelCfg)f;
+  if (M <= 128) return CFG_128x64_S6_R128;
+  if ((int64_t)tiles(M, 256) * tiles(N, 256) >= cu_count) return CFG_256_S2_R128;
+  if ((int64_t)tiles(M, 128) * tiles(N, 128) >= cu_count / 2) return CFG_128_S4_R128;
+  return CFG_128x64_S6_R128;
 }
 
 KernelCfg choose_config(int64_t M, int64_t N, int cu_count) {
@@ -180,18 +197,32 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   args.col_scale = cs;
   args.M = (int)M;
   args.N = (int)N;
+  // bytes per operand row: fp16 2K, packed int4 K/2, int8 and E3M2 K
   const int64_t row_bytes = KIND == KIND_F16 ? 2 * K : (KIND == KIND_I4 ? K / 2 : K);
   args.row_bytes = (int)row_bytes;
 
-  const KernelCfg cfg = choose_config(M, N, dev.cu_count);
+  const KernelCfg cfg = KIND == KIND_I4_E3M2 ? choose_config_e3m2(M, N, dev.cu_count)
+                                             : choose_config(M, N, dev.cu_count);
   const int64_t stage_bytes = (KIND == KIND_I4 && expands_int4_in_lds(cfg)) ? K : row_bytes;
   (void)is_skinny;
   const int rowb = stage_row_bytes(cfg);
   args.k_stages = (int)((stage_bytes + rowb - 1) / rowb);
 
+  if constexpr (KIND == KIND_I4_E3M2) {
+    switch (cfg) {
+      case CFG_256_S2_R128:
+        return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
+      case CFG_128_S4_R128:
+        return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
+      default:
+        return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128>, args, 256, stream);
+    }
+  } else {
   switch (cfg) {
     case CFG_256_S2_R128:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
+    case CFG_128_S4_R128:
+      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
     case CFG_256_S4_R64:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 4, 64>, args, 256, stream);
     case CFG_256_S3_R64:
@@ -235,6 +266,7 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     default:
       return launch<64, 64>((const void*)&gemm_tiled<KIND, 64, 64, 2, 2>, args, 256, stream);
   }
+  }
 }
 
 }  // namespace
@@ -252,6 +284,30 @@ lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A, const 
 lpgemm_status lpgemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t* A_packed,
                         const uint8_t* B_packed, int32_t* C, hipStream_t stream) {
   return run<KIND_I4>(M, N, K, A_packed, B_packed, C, nullptr, nullptr, stream);
+}
+
+lpgemm_status lpgemm_i4_to_e3m2(int64_t rows, int64_t K, const uint8_t* src_packed, uint8_t* dst,
+                                hipStream_t stream) {
+  if (rows < 0 || K < 0) return LPGEMM_ERROR_INVALID_VALUE;
+  if (K % 32 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  if (rows == 0 || K == 0) return LPGEMM_SUCCESS;
+  if (!src_packed || !dst) return LPGEMM_ERROR_INVALID_VALUE;
+  if (!aligned16(src_packed) || !aligned16(dst)) return LPGEMM_ERROR_MISALIGNED;
+  DeviceInfo dev;
+  lpgemm_status st = current_device(dev);
+  if (st != LPGEMM_SUCCESS) return st;
+  int64_t groups = rows * (K / 32);   // 32 values: 16 bytes in, 32 bytes out
+  const int64_t blocks = (groups + 255) / 256;
+  if (blocks > INT32_MAX) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  void* kargs[] = {&src_packed, &dst, &groups};
+  hipError_t e = hipLaunchKernel((const void*)&pack_i4_e3m2, dim3((unsigned)blocks), dim3(256), kargs, 0,
+                                 stream);
+  return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
+}
+
+lpgemm_status lpgemm_i4_e3m2(int64_t M, int64_t N, int64_t K, const uint8_t* A_e3m2,
+                             const uint8_t* B_e3m2, int32_t* C, hipStream_t stream) {
+  return run<KIND_I4_E3M2>(M, N, K, A_e3m2, B_e3m2, C, nullptr, nullptr, stream);
 }
 
 lpgemm_status lpgemm_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, float* C,

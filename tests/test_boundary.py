@@ -20,7 +20,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = b.declared_functions()
     assert set(names) == {"lpgemm_i8", "lpgemm_i4", "lpgemm_f16", "lpgemm_i8_dequant",
-                          "lpgemm_quantize_rows_f16", "lpgemm_status_string", "lpgemm_version"}
+                          "lpgemm_quantize_rows_f16", "lpgemm_i4_to_e3m2", "lpgemm_i4_e3m2",
+                          "lpgemm_status_string", "lpgemm_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -33,12 +34,13 @@ def test_version_and_strings(lib):
 
 
 def _call(lib, name, M, N, K, A=FAKE, B=FAKE, C=FAKE, rs=FAKE, cs=FAKE):
+    # lpgemm_i4_e3m2 has lpgemm_i4's signature and rules
     if name == "lpgemm_i8_dequant":
         return lib.lpgemm_i8_dequant(M, N, K, A, B, rs, cs, C, None)
     return getattr(lib, name)(M, N, K, A, B, C, None)
 
 
-ALL = ENTRY + ("lpgemm_i8_dequant",)
+ALL = ENTRY + ("lpgemm_i8_dequant", "lpgemm_i4_e3m2")
 K_OK = {"lpgemm_i8": 64, "lpgemm_i4": 64, "lpgemm_f16": 64, "lpgemm_i8_dequant": 64}
 
 
@@ -53,6 +55,7 @@ def test_negative_sizes(lib, name):
     ("lpgemm_i8", [8, 17, 131072, 131088]),
     ("lpgemm_i8_dequant", [8, 24, 131072]),
     ("lpgemm_i4", [16, 48, 131072, 131104]),
+    ("lpgemm_i4_e3m2", [16, 48, 131072, 131104]),
     ("lpgemm_f16", [4, 12, 1048584]),
 ])
 def test_unsupported_k(lib, name, bad_k):
@@ -142,3 +145,17 @@ def test_quantize_validation(lib):
     assert q(4, 64, MISALIGNED, FAKE, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
     assert q(4, 64, FAKE, MISALIGNED, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
     assert q(4, 64, FAKE, FAKE, FAKE + 2, None) == b.LPGEMM_ERROR_MISALIGNED
+
+
+def test_i4_to_e3m2_validation(lib):
+    f = lib.lpgemm_i4_to_e3m2
+    assert f(-1, 64, FAKE, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, -32, FAKE, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 48, FAKE, FAKE, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    assert f(4, 131104, FAKE, FAKE, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    assert f(0, 64, None, None, None) == b.LPGEMM_SUCCESS       # empty: no-op
+    assert f(4, 0, None, None, None) == b.LPGEMM_SUCCESS
+    assert f(4, 64, None, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 64, FAKE, None, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 64, MISALIGNED, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
+    assert f(4, 64, FAKE, MISALIGNED, None) == b.LPGEMM_ERROR_MISALIGNED

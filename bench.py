@@ -339,6 +339,44 @@ def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
     return w, rec
 
 
+# the kernel each square workload runs at 8192 (configuration 0)
+TRAFFIC_KERNELS = {"i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128>(lpgemm::GemmArgs)",
+                   "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128>(lpgemm::GemmArgs)",
+                   "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128>(lpgemm::GemmArgs)"}
+
+
+def _median_counter(path: str, kernel: str, counter: str) -> float:
+    import csv
+    vals = sorted(float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                  if r["Kernel_Name"] == kernel and r["Counter_Name"] == counter)
+    if not vals:
+        raise SystemExit(f"{path}: no {counter} rows for {kernel}")
+    return vals[len(vals) // 2]
+
+
+def write_traffic(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
+                  copy_mib: int) -> dict:
+    """profiles/traffic.json from rocprofv3 --pmc counter CSVs: per launch,
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median) of each 8192
+    workload's kernel, scaled by the ratio of a plain device copy's known
+    bytes to what the same counter reads for it."""
+    copy_kib = copy_mib * 1024.0
+    copy_kernel = "__amd_rocclr_copyBuffer"
+    fetch_scale = copy_kib / _median_counter(copy_fetch_csv, copy_kernel, "FETCH_SIZE")
+    write_scale = copy_kib / _median_counter(copy_write_csv, copy_kernel, "WRITE_SIZE")
+    out = {}
+    for name, kernel in TRAFFIC_KERNELS.items():
+        f = _median_counter(fetch_csv, kernel, "FETCH_SIZE")
+        w = _median_counter(write_csv, kernel, "WRITE_SIZE")
+        out[name] = {"fetch_bytes": int(f * 1024 * fetch_scale), "write_bytes": int(w * 1024 * write_scale),
+                     "fetch_kib_raw": f, "write_kib_raw": w, "fetch_scale": round(fetch_scale, 5),
+                     "write_scale": round(write_scale, 5), "kernel_source_hash": kernel_source_hash(),
+                     "kernel": kernel}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,7 +396,17 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (--steps times); its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the traffic figures")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                         "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc counter CSVs of this "
+                         "benchmark's default run and of --copy-calibration (no GPU needed)")
+    ap.add_argument("--copy-mib", type=int, default=256,
+                    help="size of the copy the calibration CSVs were taken on")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        print(json.dumps(write_traffic(*args.write_traffic, args.copy_mib), indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "

@@ -1,9 +1,10 @@
 // MFMA-only ceiling of the GPU at its sustained clock.
 //
-// Runs back-to-back kernels that issue only 32x32 MFMAs (int8 32x32x32 or
-// fp16 32x32x16) on pseudo-random register operands, eight independent
-// accumulators per wave, two waves per SIMD, for a given number of seconds,
-// and prints the achieved rate.  No memory traffic, so this is the upper
+// Runs back-to-back kernels that issue only 32x32 MFMAs (int8 32x32x32,
+// fp16 32x32x16, and the 32x32x64 f8f6f4 MFMA with FP8 E4M3, FP6 E3M2 and
+// FP4 E2M1 operands) on pseudo-random register operands, eight independent
+// accumulators per wave, two waves per SIMD, for a given number of seconds
+// each, and prints the achieved rates.  No memory traffic, so this is the upper
 // bound a GEMM kernel can reach at the clock the board sustains under MFMA
 // load (which is below the 2.4 GHz the datasheet peaks assume).
 //
@@ -18,6 +19,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kChains = 8;
 
@@ -69,6 +71,35 @@ __global__ __launch_bounds__(256) void mfma_f16(int iters, int* out, unsigned se
   out[blockIdx.x * blockDim.x + threadIdx.x] = (int)s;
 }
 
+// FMT: 0 FP8 E4M3, 3 FP6 E3M2, 4 FP4 E2M1 (the f8f6f4 format codes); block
+// scales 2^0.  Operand bytes are random six-bit values (for FP8 that keeps
+// every code finite), so FP6 sees every E3M2 code.
+template <int FMT>
+__global__ __launch_bounds__(256) void mfma_f8f6f4(int iters, int* out, unsigned seed) {
+  unsigned x = (threadIdx.x + 1) * 2654435761u ^ seed;
+  i32x8 a[4], b[4];
+  for (int i = 0; i < 4; ++i)
+    for (int e = 0; e < 8; ++e) {
+      x = x * 1664525u + 1013904223u;
+      a[i][e] = (int)(x & 0x3f3f3f3fu);
+      x = x * 1664525u + 1013904223u;
+      b[i][e] = (int)(x & 0x3f3f3f3fu);
+    }
+  f32x16 c[kChains] = {};
+  for (int it = 0; it < iters; it += 4) {
+#pragma unroll
+    for (int rot = 0; rot < 4; ++rot)
+#pragma unroll
+      for (int j = 0; j < kChains; ++j)
+        c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 3], b[(j + rot) & 3], c[j], FMT, FMT,
+                                                               0, 127, 0, 127);
+  }
+  float s = 0;
+  for (int j = 0; j < kChains; ++j)
+    for (int e = 0; e < 16; ++e) s += c[j][e];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = (int)s;
+}
+
 template <typename Kernel>
 double sustained(Kernel k, double seconds, double macs_per_wave_iter, int cus, int* out) {
   const int blocks = cus * 2;   // 256 threads each: two waves per SIMD
@@ -100,9 +131,13 @@ int main(int argc, char** argv) {
   if (hipMalloc(&out, (size_t)prop.multiProcessorCount * 2 * 256 * sizeof(int)) != hipSuccess) return 1;
   const double i8 = sustained(mfma_i8, seconds, 32.0 * 32 * 32, prop.multiProcessorCount, out);
   const double f16 = sustained(mfma_f16, seconds, 32.0 * 32 * 16, prop.multiProcessorCount, out);
+  const double e3m2 = sustained(mfma_f8f6f4<3>, seconds, 32.0 * 32 * 64, prop.multiProcessorCount, out);
+  const double fp8 = sustained(mfma_f8f6f4<0>, seconds, 32.0 * 32 * 64, prop.multiProcessorCount, out);
+  const double fp4 = sustained(mfma_f8f6f4<4>, seconds, 32.0 * 32 * 64, prop.multiProcessorCount, out);
   printf("{\"device\": \"%s\", \"cus\": %d, \"seconds_each\": %.1f, "
-         "\"mfma_i8_tops\": %.1f, \"mfma_f16_tflops\": %.1f}\n",
-         prop.gcnArchName, prop.multiProcessorCount, seconds, i8, f16);
+         "\"mfma_i8_tops\": %.1f, \"mfma_f16_tflops\": %.1f, \"mfma_fp6_e3m2_tflops\": %.1f, "
+         "\"mfma_fp8_tflops\": %.1f, \"mfma_fp4_tflops\": %.1f}\n",
+         prop.gcnArchName, prop.multiProcessorCount, seconds, i8, f16, e3m2, fp8, fp4);
   (void)hipFree(out);
-  return (i8 > 0 && f16 > 0) ? 0 : 1;
+  return (i8 > 0 && f16 > 0 && e3m2 > 0 && fp8 > 0 && fp4 > 0) ? 0 : 1;
 }

@@ -377,17 +377,28 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // LDS byte address lds_addr + 16 l.  M0 carries the LDS address for the
 // load and is restored afterwards; one wait state separates the M0 write
 // from its use.
+// Cache policy of the operand loads (the gfx950 cache-policy bits, written
+// before `lds`): 0 default, 1 nt (non-temporal: stream, evict first),
+// 2 sc0, 3 sc1, 4 sc0 sc1 (widest coherence scope).
+template <int CPOL = 0>
 __device__ __forceinline__ void lds_dma_16(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_addr), "v"(voff), "s"(rsrc)
-      : "memory");
+#define LPGEMM_LDS_DMA(MODS)                                              \
+  asm volatile(                                                           \
+      "s_mov_b32 %0, m0\n\t"                                              \
+      "s_mov_b32 m0, %1\n\t"                                              \
+      "s_nop 0\n\t"                                                       \
+      "buffer_load_dwordx4 %2, %3, 0 offen " MODS "lds\n\t"              \
+      "s_mov_b32 m0, %0"                                                  \
+      : "=&s"(saved)                                                      \
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)                               \
+      : "memory")
+  if constexpr (CPOL == 1) LPGEMM_LDS_DMA("nt ");
+  else if constexpr (CPOL == 2) LPGEMM_LDS_DMA("sc0 ");
+  else if constexpr (CPOL == 3) LPGEMM_LDS_DMA("sc1 ");
+  else if constexpr (CPOL == 4) LPGEMM_LDS_DMA("sc0 sc1 ");
+  else LPGEMM_LDS_DMA("");
+#undef LPGEMM_LDS_DMA
 }
 
 template <int N>
@@ -459,7 +470,10 @@ struct RowLayout<64> {
   __device__ static int pos(int r, int c) { return c ^ f(r); }
 };
 
-template <int KIND, int BM, int BN, int STAGES, int ROWB>
+// CPOL: cache policy of the operand loads (see lds_dma_16).  SPLIT: waves 0
+// and 1 load only A, waves 2 and 3 only B (needs BM == BN); by default every
+// wave loads its share of both.  These two are ablation knobs.
+template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false>
 __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
@@ -510,24 +524,36 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   // Load slot t of this wave fills stage rows kRowsPerLoad*g .. (g = 4t +
   // wave): lane l writes row kRowsPerLoad*g + l / kChunks at chunk position
   // l % kChunks, so it fetches the global chunk whose swizzled position that is.
+  static_assert(!SPLIT || BM == BN, "a split loader gives A and B the same number of waves");
+  // slot t of this wave loads row group g (kRowsPerLoad rows; A's groups
+  // come first); interleaved: g = 4t + wave, split: waves 0-1 walk A's
+  // groups, waves 2-3 B's
+  auto group_of = [&](int t) -> int {
+    if constexpr (SPLIT) return wave < 2 ? 2 * t + wave : BM / kRowsPerLoad + 2 * t + (wave - 2);
+    else return 4 * t + wave;
+  };
+  auto is_a = [&](int t) -> bool {
+    if constexpr (SPLIT) return wave < 2;
+    else return t < kSlotsA;
+  };
   uint32_t slot_off[kSlots];
   uint32_t slot_col[kSlots];
 #pragma unroll
   for (int t = 0; t < kSlots; ++t) {
-    const int g = 4 * t + wave;
+    const int g = group_of(t);
     const int lrow = kRowsPerLoad * g + lane / Layout::kChunks;
     const int c = Layout::pos(lrow, lane % Layout::kChunks);   // XOR swizzle is an involution
-    const int grow = t < kSlotsA ? lrow : lrow - BM;
+    const int grow = is_a(t) ? lrow : lrow - BM;
     slot_off[t] = grow * p.row_bytes + c * 16;
     slot_col[t] = c * 16;
   }
 
   auto issue_load = [&](int t, int s) {
     const uint32_t kbyte = (uint32_t)s * ROWB;
-    const int g = 4 * t + wave;
+    const int g = group_of(t);
     const bool in_row = kbyte + slot_col[t] < (uint32_t)p.row_bytes;
     const uint32_t off = in_row ? slot_off[t] + kbyte : kOutOfRange;
-    lds_dma_16(t < kSlotsA ? rsrc_a : rsrc_b, smem_lds + (s % STAGES) * kStage + g * 1024, off);
+    lds_dma_16<CPOL>(is_a(t) ? rsrc_a : rsrc_b, smem_lds + (s % STAGES) * kStage + g * 1024, off);
   };
 
   // Fragment addressing: lane l reads row (l & 31) of a 32-row block; blocks

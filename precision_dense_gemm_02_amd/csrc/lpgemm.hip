@@ -109,7 +109,12 @@ enum KernelCfg {
   CFG_128x64_S6_R128 = 20,    // 4 waves, 128 x 64, 6 stages of 128-byte rows
   CFG_128x64_S8_R64 = 21,     // 4 waves, 128 x 64, 8 stages of 64-byte rows
   CFG_128_S4_R128 = 22,       // 4 waves, 128 x 128, 4 stages of 128-byte rows
-  CFG_COUNT = 23
+  // ablations of configuration 0
+  CFG_256_S2_R128_NT = 23,       // operand loads non-temporal (nt)
+  CFG_256_S2_R128_SC0 = 24,      // operand loads sc0
+  CFG_256_S2_R128_SC01 = 25,     // operand loads sc0 sc1
+  CFG_256_S2_R128_SPLIT = 26,    // split loader: two waves load A, two load B
+  CFG_COUNT = 27
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -263,6 +268,14 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128>, args, 256, stream);
     case CFG_128x64_S8_R64:
       return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 8, 64>, args, 256, stream);
+    case CFG_256_S2_R128_NT:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 1>, args, 256, stream);
+    case CFG_256_S2_R128_SC0:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 2>, args, 256, stream);
+    case CFG_256_S2_R128_SC01:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 4>, args, 256, stream);
+    case CFG_256_S2_R128_SPLIT:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, true>, args, 256, stream);
     default:
       return launch<64, 64>((const void*)&gemm_tiled<KIND, 64, 64, 2, 2>, args, 256, stream);
   }

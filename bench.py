@@ -39,11 +39,12 @@ METRIC = "INT8/INT4 TOPS and FP16 TFLOPS at N=8192 on 1 MI355X; % of MFMA peak"
 # Dense MFMA peaks of the MI355X (256 CUs, 2.4 GHz): int8 8192 ops and fp16
 # 4096 flops per CU per clock.  INT4 runs on the int8 MFMA.
 PEAK_TOPS = {"i8": 5033.2, "i4": 5033.2, "dq": 5033.2, "w8": 5033.2, "f16": 2516.6,
-             "i4e": 5033.2, "i4g": 5033.2}
+             "i4e": 5033.2, "i4g": 5033.2, "i8kn": 5033.2}
 HBM_PEAK_GBS = 8000.0
 UNIT = {"i8": "TOPS", "i4": "TOPS", "dq": "TOPS", "w8": "TOPS", "f16": "TFLOPS", "i4e": "TOPS",
-        "i4g": "TOPS"}
-DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "w8": "i8", "f16": "f16", "i4e": "i4", "i4g": "i4"}
+        "i4g": "TOPS", "i8kn": "TOPS"}
+DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "w8": "i8", "f16": "f16", "i4e": "i4", "i4g": "i4",
+         "i8kn": "i8"}
 KERNEL_SOURCES = ["precision_dense_gemm_02_amd/csrc/gemm_kernels.hpp",
                   "precision_dense_gemm_02_amd/csrc/lpgemm.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -66,7 +67,7 @@ def parse_workload(name: str):
     if kind == "w8a8":
         from precision_dense_gemm_02_amd import inputs
         return "w8", size, inputs.LLM_N, inputs.LLM_K
-    if kind not in ("i8", "i4", "f16", "i4e", "i4g"):
+    if kind not in ("i8", "i4", "f16", "i4e", "i4g", "i8kn"):
         raise SystemExit(f"unknown workload {name}")
     return kind, size, size, size
 
@@ -97,6 +98,16 @@ class Workload:
             a, b = to(p.a), to(p.b_t)
             out = torch.empty((M, N), dtype=torch.int32, device=dev)
             self.launch = lambda i: lp.gemm_i8(a, b, out=out)
+            self.in_bytes = M * K + N * K
+            self.out_bytes = 4 * M * N
+        elif kind == "i8kn":
+            # the int8 workload with B stored K x N row-major (N contiguous)
+            self.seed = inputs.seed_for("i8", M)
+            p = inputs.int8_problem(M, N, K, self.seed)
+            self.host = p
+            a, b_kxn = to(p.a), to(np.ascontiguousarray(p.b_t.T))
+            out = torch.empty((M, N), dtype=torch.int32, device=dev)
+            self.launch = lambda i: lp.gemm_i8_kxn(a, b_kxn, out=out)
             self.in_bytes = M * K + N * K
             self.out_bytes = 4 * M * N
         elif kind == "i4":
@@ -183,7 +194,7 @@ class Workload:
         rows = sorted(set([0, self.M - 1] + rng.choice(self.M, min(nrows, self.M), replace=False).tolist()))
         got = self.out.cpu().numpy()[rows]
         p = self.host
-        if self.kind == "i8":
+        if self.kind in ("i8", "i8kn"):
             ok = np.array_equal(got, oracle.gemm_i8(p.a, p.b_t, rows=rows))
         elif self.kind in ("i4", "i4e", "i4g"):
             ok = np.array_equal(got, oracle.gemm_i4(p.a_packed, p.b_packed, self.K, rows=rows))
@@ -288,7 +299,7 @@ def cpu_baseline(w: Workload, seconds: float) -> dict:
 
     def run(rows):
         t0 = time.perf_counter()
-        if w.kind == "i8":
+        if w.kind in ("i8", "i8kn"):
             oracle.gemm_i8(p.a, p.b_t, rows=rows)
         elif w.kind in ("i4", "i4e", "i4g"):
             oracle.gemm_i4(p.a_packed, p.b_packed, w.K, rows=rows)

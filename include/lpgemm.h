@@ -94,6 +94,15 @@ lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, const 
 lpgemm_status lpgemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A_packed,
                         const uint8_t *B_packed, int32_t *C, hipStream_t stream);
 
+/* INT8 with B stored K x N row-major (N contiguous; the "transposed" B of
+ * the PTX-vs-WMMA summary page's layout ablation): C = A . B exactly in
+ * int32, as lpgemm_i8.  A: M x K int8, B_kxn: K x N int8, C: M x N int32.
+ * K must be a multiple of 16 and at most LPGEMM_MAX_K_INT; N a multiple of
+ * 16 (every k-row starts 16-byte aligned) with K * N < 2^31.  Pointers
+ * 16-byte aligned.  Errors and degenerate sizes as for lpgemm_i8. */
+lpgemm_status lpgemm_i8_kxn(int64_t M, int64_t N, int64_t K, const int8_t *A, const int8_t *B_kxn,
+                            int32_t *C, hipStream_t stream);
+
 /* INT4 through FP6 E3M2 matrix cores, step 1 of 2: re-encode packed int4
  * rows (the layout of lpgemm_i4: two values per byte along k, low nibble =
  * even k, two's complement) as E3M2 operand rows.  Every value in [-8, 7] is

@@ -9,9 +9,9 @@ the torch-facing binding (see _binding.py), the in-tree build step (build.py)
 and the seeded input generators (inputs.py).
 """
 from ._binding import (LpgemmError, gemm_f16, gemm_i4, gemm_i4_e3m2, gemm_i4_via_e3m2,  # noqa: F401
-                       gemm_i8, gemm_i8_dequant, i4_to_e3m2, load_library, quantize_rows_f16,
+                       gemm_i8, gemm_i8_dequant, gemm_i8_kxn, i4_to_e3m2, load_library, quantize_rows_f16,
                        status_string, version, w8a8_linear)
 
-__all__ = ["LpgemmError", "gemm_i8", "gemm_i4", "gemm_f16", "gemm_i8_dequant",
+__all__ = ["LpgemmError", "gemm_i8", "gemm_i8_kxn", "gemm_i4", "gemm_f16", "gemm_i8_dequant",
            "quantize_rows_f16", "w8a8_linear", "i4_to_e3m2", "gemm_i4_e3m2", "gemm_i4_via_e3m2",
            "load_library", "status_string", "version"]

@@ -61,6 +61,8 @@ def load_library():
         lib.lpgemm_i8_dequant.restype = ctypes.c_int
         lib.lpgemm_quantize_rows_f16.argtypes = [_i64, _i64, _p, _p, _p, _p]
         lib.lpgemm_quantize_rows_f16.restype = ctypes.c_int
+        lib.lpgemm_i8_kxn.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p]
+        lib.lpgemm_i8_kxn.restype = ctypes.c_int
         lib.lpgemm_i4_to_e3m2.argtypes = [_i64, _i64, _p, _p, _p]
         lib.lpgemm_i4_to_e3m2.restype = ctypes.c_int
         lib.lpgemm_i4_e3m2.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p]
@@ -153,6 +155,24 @@ def gemm_i8(a, b_t, out=None):
     with torch.cuda.device(dev):
         _check(load_library().lpgemm_i8(M, N, K, a.data_ptr(), b_t.data_ptr(), out.data_ptr(),
                                         _stream_handle(dev)), "lpgemm_i8")
+    return out
+
+
+def gemm_i8_kxn(a, b_kxn, out=None):
+    """int32 C = A . B with B stored K x N row-major (N contiguous); a: M x K
+    int8, b_kxn: K x N int8."""
+    torch = _torch()
+    _operand(a, torch.int8, "a")
+    _operand(b_kxn, torch.int8, "b_kxn")
+    if a.shape[1] != b_kxn.shape[0]:
+        raise ValueError(f"K mismatch: a {tuple(a.shape)}, b_kxn {tuple(b_kxn.shape)}")
+    dev = _same_device(a, b_kxn)
+    M, K = a.shape
+    N = b_kxn.shape[1]
+    out = _output(out, (M, N), torch.int32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_i8_kxn(M, N, K, a.data_ptr(), b_kxn.data_ptr(), out.data_ptr(),
+                                            _stream_handle(dev)), "lpgemm_i8_kxn")
     return out
 
 

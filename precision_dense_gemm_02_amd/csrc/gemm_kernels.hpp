@@ -473,7 +473,20 @@ struct RowLayout<64> {
 // CPOL: cache policy of the operand loads (see lds_dma_16).  SPLIT: waves 0
 // and 1 load only A, waves 2 and 3 only B (needs BM == BN); by default every
 // wave loads its share of both.  These two are ablation knobs.
-template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false>
+//
+// BKN: B is stored K x N row-major (N contiguous, int8) instead of
+// K-contiguous.  A stage then holds ROWB k-rows of the tile's BN columns of
+// B, copied with the same coalesced 1 KiB direct-to-LDS loads (16 lanes per
+// 256-byte k-row), and the MFMA's B fragments are read back transposed with
+// ds_read_b64_tr_b8.  Within each group of 16 lanes that instruction gives
+// lane 8h + c byte c of the eight 8-byte rows addressed by lanes 2b + h
+// (b = 0..7); so lane l, addressing k-row 16 (l/32) + b (+8 for the second
+// read) at columns (l/16 % 2) 16 + 8h, receives 8 consecutive k of column
+// l % 32, in the k order of the A fragment.  16-byte chunks of k-row k are
+// XOR-swizzled by 2k, which puts the eight rows one read touches on
+// distinct banks.
+template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false,
+          bool BKN = false>
 __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
@@ -486,6 +499,8 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   // the two fragment buffers alternate per K-step and the next stage's first
   // step reads into buffer 0 again, so a stage needs an even number of steps
   static_assert(KSTEPS % 2 == 0, "K-steps per stage must be even");
+  static_assert(!BKN || KIND == KIND_I8 || KIND == KIND_I8_DEQUANT, "K x N storage of B is int8 only");
+  static_assert(!BKN || !SPLIT, "one ablation at a time");
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM % 2 == 0 && TN >= 1 && BM % 128 == 0 && BN % 64 == 0, "tile");
@@ -518,7 +533,10 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   const int rows_a = min(BM, p.M - m0);
   const int rows_b = min(BN, p.N - n0);
   const i32x4 rsrc_a = make_rsrc(p.A + (size_t)m0 * p.row_bytes, rows_a * p.row_bytes);
-  const i32x4 rsrc_b = make_rsrc(p.B + (size_t)n0 * p.row_bytes, rows_b * p.row_bytes);
+  // K-contiguous B: this tile's BN rows; K x N B: the whole matrix (K rows of
+  // N bytes, below 2^31 bytes), columns selected per lane
+  const i32x4 rsrc_b = BKN ? make_rsrc(p.B, (uint32_t)p.row_bytes * (uint32_t)p.N)
+                           : make_rsrc(p.B + (size_t)n0 * p.row_bytes, rows_b * p.row_bytes);
   const uint32_t smem_lds = lds_address(smem);
 
   // Load slot t of this wave fills stage rows kRowsPerLoad*g .. (g = 4t +
@@ -536,23 +554,44 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     if constexpr (SPLIT) return wave < 2;
     else return t < kSlotsA;
   };
+  // K x N B: 16-byte chunks per k-row of the tile, and the chunk swizzle
+  constexpr int kBChunks = BN / 16;
+  auto b_swz = [](int krow) -> int { return (2 * krow) & (kBChunks - 1); };
   uint32_t slot_off[kSlots];
-  uint32_t slot_col[kSlots];
+  uint32_t slot_col[kSlots];   // K-contiguous rows: byte column; K x N B: k-row in the stage
+  bool slot_ok[kSlots];        // K x N B: the chunk's columns lie inside N
 #pragma unroll
   for (int t = 0; t < kSlots; ++t) {
     const int g = group_of(t);
-    const int lrow = kRowsPerLoad * g + lane / Layout::kChunks;
-    const int c = Layout::pos(lrow, lane % Layout::kChunks);   // XOR swizzle is an involution
-    const int grow = is_a(t) ? lrow : lrow - BM;
-    slot_off[t] = grow * p.row_bytes + c * 16;
-    slot_col[t] = c * 16;
+    if (BKN && !is_a(t)) {
+      const int krow = (g - BM / kRowsPerLoad) * (1024 / BN) + lane / kBChunks;
+      const int c = (lane % kBChunks) ^ b_swz(krow);
+      const int col = n0 + c * 16;
+      slot_off[t] = (uint32_t)krow * (uint32_t)p.N + col;
+      slot_col[t] = krow;
+      slot_ok[t] = col < p.N;
+    } else {
+      const int lrow = kRowsPerLoad * g + lane / Layout::kChunks;
+      const int c = Layout::pos(lrow, lane % Layout::kChunks);   // XOR swizzle is an involution
+      const int grow = is_a(t) ? lrow : lrow - BM;
+      slot_off[t] = grow * p.row_bytes + c * 16;
+      slot_col[t] = c * 16;
+      slot_ok[t] = true;
+    }
   }
 
   auto issue_load = [&](int t, int s) {
     const uint32_t kbyte = (uint32_t)s * ROWB;
     const int g = group_of(t);
-    const bool in_row = kbyte + slot_col[t] < (uint32_t)p.row_bytes;
-    const uint32_t off = in_row ? slot_off[t] + kbyte : kOutOfRange;
+    uint32_t off;
+    if (BKN && !is_a(t)) {
+      // k-row s*ROWB + krow of B, when inside K
+      const bool ok = slot_ok[t] && kbyte + slot_col[t] < (uint32_t)p.row_bytes;
+      off = ok ? slot_off[t] + kbyte * (uint32_t)p.N : kOutOfRange;
+    } else {
+      const bool in_row = kbyte + slot_col[t] < (uint32_t)p.row_bytes;
+      off = in_row ? slot_off[t] + kbyte : kOutOfRange;
+    }
     lds_dma_16<CPOL>(is_a(t) ? rsrc_a : rsrc_b, smem_lds + (s % STAGES) * kStage + g * 1024, off);
   };
 
@@ -581,10 +620,32 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   };
   Raw fa[2][TM], fb[2][TN];
 
+  // K x N B: this lane's transposed-read addresses within the B region, per
+  // K-step and n-block (the two reads are 8 k-rows apart; the swizzle of
+  // k-row k and k + 8 is the same)
+  const int tr_b = (lane % 16) / 2, tr_h = lane % 2, tr_g = lane / 16;
+  auto b_tr_off = [&](int kk, int j) -> int {
+    const int krow = 32 * kk + 16 * (tr_g / 2) + tr_b;
+    const int ncol = wn * WTN + 32 * j + (16 * tr_g + 8 * tr_h) % 32;
+    return krow * BN + (((ncol / 16) ^ b_swz(krow)) << 4) + (ncol % 16);
+  };
+
   auto read_frags = [&](int s, int kk, int dst) {
     const uint8_t* base = smem + (s % STAGES) * kStage;
     const int off = frag_off(kk);
-    if constexpr (E3M2) {
+    if constexpr (BKN) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[dst][i] = *(const Raw*)(base + a_row_base + i * 32 * ROWB + off);
+      typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint8_t* pb = base + BM * ROWB + b_tr_off(kk, j);
+        const i32x2_t lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(lds_address(pb)));
+        const i32x2_t hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(lds_address(pb + 8 * BN)));
+        fb[dst][j] = i32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    } else if constexpr (E3M2) {
       const int off2 = frag_off2(kk);
 #pragma unroll
       for (int i = 0; i < TM; ++i)

@@ -184,9 +184,30 @@ lpgemm_status launch(const void* fn, GemmArgs args, int threads, hipStream_t str
   return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
 }
 
-template <int KIND>
+// B stored K x N row-major runs on the LDS-pipelined kernels with 128-byte
+// stage rows: 128 k-rows of B per stage.
+bool supports_kxn(int c) {
+  return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128;
+}
+
+KernelCfg choose_config_kxn(int64_t M, int64_t N, int cu_count) {
+  const int f = forced_config();
+  if (f >= 0 && supports_kxn(f)) return (KernelCfg)f;
+  if (M <= 128) return CFG_128x64_S6_R128;
+  if ((int64_t)tiles(M, 256) * tiles(N, 256) >= cu_count) return CFG_256_S2_R128;
+  if ((int64_t)tiles(M, 128) * tiles(N, 128) >= cu_count / 2) return CFG_128_S4_R128;
+  return CFG_128x64_S6_R128;
+}
+
+template <int KIND, bool BKN = false>
 lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
                   const float* rs, const float* cs, hipStream_t stream) {
+  // K x N B: k-rows of N bytes must start 16-byte aligned and the matrix
+  // must fit the 32-bit offsets of its buffer resource (a shape error, so it
+  // ranks with the K checks: after negative sizes, before pointers)
+  if (BKN && M > 0 && N > 0 && K >= 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX &&
+      (N % 16 != 0 || K * N >= ((int64_t)1 << 31)))
+    return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
   bool nothing_to_do = false;
   lpgemm_status st = validate((Kind)KIND, M, N, K, A, B, C, rs, cs, nothing_to_do);
   if (st != LPGEMM_SUCCESS || nothing_to_do) return st;
@@ -206,14 +227,27 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   const int64_t row_bytes = KIND == KIND_F16 ? 2 * K : (KIND == KIND_I4 ? K / 2 : K);
   args.row_bytes = (int)row_bytes;
 
-  const KernelCfg cfg = KIND == KIND_I4_E3M2 ? choose_config_e3m2(M, N, dev.cu_count)
+  const KernelCfg cfg = BKN ? choose_config_kxn(M, N, dev.cu_count)
+                      : KIND == KIND_I4_E3M2 ? choose_config_e3m2(M, N, dev.cu_count)
                                              : choose_config(M, N, dev.cu_count);
   const int64_t stage_bytes = (KIND == KIND_I4 && expands_int4_in_lds(cfg)) ? K : row_bytes;
   (void)is_skinny;
   const int rowb = stage_row_bytes(cfg);
   args.k_stages = (int)((stage_bytes + rowb - 1) / rowb);
 
-  if constexpr (KIND == KIND_I4_E3M2) {
+  if constexpr (BKN) {
+    switch (cfg) {
+      case CFG_256_S2_R128:
+        return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, true>, args, 256,
+                                stream);
+      case CFG_128_S4_R128:
+        return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128, 0, false, true>, args, 256,
+                                stream);
+      default:
+        return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128, 0, false, true>, args, 256,
+                               stream);
+    }
+  } else if constexpr (KIND == KIND_I4_E3M2) {
     switch (cfg) {
       case CFG_256_S2_R128:
         return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
@@ -297,6 +331,11 @@ lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A, const 
 lpgemm_status lpgemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t* A_packed,
                         const uint8_t* B_packed, int32_t* C, hipStream_t stream) {
   return run<KIND_I4>(M, N, K, A_packed, B_packed, C, nullptr, nullptr, stream);
+}
+
+lpgemm_status lpgemm_i8_kxn(int64_t M, int64_t N, int64_t K, const int8_t* A, const int8_t* B_kxn,
+                            int32_t* C, hipStream_t stream) {
+  return run<KIND_I8, true>(M, N, K, A, B_kxn, C, nullptr, nullptr, stream);
 }
 
 lpgemm_status lpgemm_i4_to_e3m2(int64_t rows, int64_t K, const uint8_t* src_packed, uint8_t* dst,

@@ -21,6 +21,7 @@ def test_exports_every_declared_symbol(lib):
     names = b.declared_functions()
     assert set(names) == {"lpgemm_i8", "lpgemm_i4", "lpgemm_f16", "lpgemm_i8_dequant",
                           "lpgemm_quantize_rows_f16", "lpgemm_i4_to_e3m2", "lpgemm_i4_e3m2",
+                          "lpgemm_i8_kxn",
                           "lpgemm_status_string", "lpgemm_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -34,13 +35,16 @@ def test_version_and_strings(lib):
 
 
 def _call(lib, name, M, N, K, A=FAKE, B=FAKE, C=FAKE, rs=FAKE, cs=FAKE):
-    # lpgemm_i4_e3m2 has lpgemm_i4's signature and rules
+    # lpgemm_i4_e3m2 has lpgemm_i4's signature and rules; lpgemm_i8_kxn
+    # lpgemm_i8's, plus N % 16 == 0 (the generic cases use N = 4 -> 16)
+    if name == "lpgemm_i8_kxn" and N == 4:
+        N = 16
     if name == "lpgemm_i8_dequant":
         return lib.lpgemm_i8_dequant(M, N, K, A, B, rs, cs, C, None)
     return getattr(lib, name)(M, N, K, A, B, C, None)
 
 
-ALL = ENTRY + ("lpgemm_i8_dequant", "lpgemm_i4_e3m2")
+ALL = ENTRY + ("lpgemm_i8_dequant", "lpgemm_i4_e3m2", "lpgemm_i8_kxn")
 K_OK = {"lpgemm_i8": 64, "lpgemm_i4": 64, "lpgemm_f16": 64, "lpgemm_i8_dequant": 64}
 
 
@@ -56,6 +60,7 @@ def test_negative_sizes(lib, name):
     ("lpgemm_i8_dequant", [8, 24, 131072]),
     ("lpgemm_i4", [16, 48, 131072, 131104]),
     ("lpgemm_i4_e3m2", [16, 48, 131072, 131104]),
+    ("lpgemm_i8_kxn", [8, 17, 131072, 131088]),
     ("lpgemm_f16", [4, 12, 1048584]),
 ])
 def test_unsupported_k(lib, name, bad_k):
@@ -159,3 +164,16 @@ def test_i4_to_e3m2_validation(lib):
     assert f(4, 64, FAKE, None, None) == b.LPGEMM_ERROR_INVALID_VALUE
     assert f(4, 64, MISALIGNED, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
     assert f(4, 64, FAKE, MISALIGNED, None) == b.LPGEMM_ERROR_MISALIGNED
+
+
+def test_kxn_shape_rules(lib):
+    f = lib.lpgemm_i8_kxn
+    # N must be a multiple of 16 (16-byte aligned k-rows) and K * N < 2^31
+    assert f(4, 40, 64, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    assert f(4, 32768, 65536, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    # a shape error ranks before pointer errors, after negative sizes
+    assert f(4, 40, 64, None, None, None, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    assert f(-4, 40, 64, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    # M = 0 or N = 0 is still a no-op
+    assert f(0, 40, 64, None, None, None, None) == b.LPGEMM_SUCCESS
+    assert f(4, 0, 64, None, None, None, None) == b.LPGEMM_SUCCESS

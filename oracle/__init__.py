@@ -32,8 +32,8 @@ class OracleError(RuntimeError):
 
 
 _STATUS = {1: "integer result does not fit int32",
-           2: "fp16 operand is inf or NaN",
-           3: "bad row range or odd K"}
+           2: "fp16 or fp64 operand is inf or NaN",
+           3: "bad row range, odd K or target bits outside [1, 53]"}
 
 
 def build(force: bool = True) -> str:
@@ -64,6 +64,8 @@ def _configure(lib):
     lib.oracle_f16_decode.restype = ctypes.c_double
     lib.oracle_quantize_rows_f16.argtypes = [_i64, _i64, _p, _p, _p, _i64, _i64]
     lib.oracle_quantize_rows_f16.restype = ctypes.c_int
+    lib.oracle_f64_emu.argtypes = [_i64, _i64, _i64, _p, _p, ctypes.c_int, _p, _i64, _i64]
+    lib.oracle_f64_emu.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -200,6 +202,22 @@ def quantize_rows_f16(X: np.ndarray, rows=None):
     if not qs:
         return np.empty((0, K), np.int8), np.empty(0, np.float32)
     return np.concatenate(qs, axis=0), np.concatenate(ss)
+
+
+def f64_emu(A: np.ndarray, B_t: np.ndarray, bits: int, rows=None) -> np.ndarray:
+    """fp64 product through scaled integers: rows of A and rows of B_t (the
+    columns of B) scaled by powers of two to integers of at most `bits`
+    bits (nearest, ties to even), multiplied exactly, converted to double
+    once and scaled back.  A: M x K float64, B_t: N x K float64."""
+    A = _c(A, np.float64)
+    B_t = _c(B_t, np.float64)
+    M, K = A.shape
+    N = B_t.shape[0]
+    assert B_t.shape[1] == K
+    lib = _load()
+    (C,) = _run_rows(lambda *a: lib.oracle_f64_emu(M, N, K, _ptr(A), _ptr(B_t), int(bits), *a),
+                     M, N, rows, [np.float64])
+    return C
 
 
 def f16_decode(bits: int):

@@ -30,6 +30,20 @@
  *                   nearest-even integer to x / scale computed in binary32,
  *                   clamped to [-127, 127]; an all-zero row gets scale 0 and
  *                   q = 0.
+ *   fp64 emulation: the fp64 product through integer GEMMs (the day-12 page
+ *                   of the FP64-emulation series: scale/exponent scan, then
+ *                   integer products, then undo the scaling).  The pages
+ *                   leave the scaling rule open; the plainest reading, with t
+ *                   the target bits: each row of A (each column of B) is
+ *                   multiplied by 2^(t - e), e the binary exponent of its
+ *                   largest magnitude (max = f 2^e, 0.5 <= f < 1), and
+ *                   rounded to the nearest integer (ties to even), so
+ *                   |a'| <= 2^t.  X = A'.B' is summed exactly (128-bit
+ *                   integers), converted to double with one rounding, and
+ *                   scaled by 2^-(2t - eA[i] - eB[j]).  How the GPU obtains
+ *                   X (residues modulo several moduli and the Chinese
+ *                   remainder theorem) does not change the value, so this
+ *                   oracle takes the direct product.
  *
  * Layouts: A is M x K row-major; B is stored K-contiguous (N rows of K);
  * C is M x N row-major.  Every entry point computes the output rows
@@ -42,12 +56,14 @@
  * in increasing k.
  *
  * Return value: 0 on success; 1 if an integer result does not fit int32
- * (the input is outside the library's contract); 2 if an fp16 operand is
- * inf or NaN (outside the contract); 3 for a bad row range.
+ * (the input is outside the library's contract); 2 if an fp16 or fp64
+ * operand is inf or NaN (outside the contract); 3 for a bad row range or a
+ * target bit count outside [1, 53].
  */
 #include <stdint.h>
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -247,6 +263,71 @@ int oracle_quantize_rows_f16(int64_t M, int64_t K, const uint16_t *X, int8_t *Q,
         }
     }
     return status;
+}
+
+/* Binary exponent of the largest magnitude of n doubles (frexp convention:
+ * max = f 2^e with 0.5 <= f < 1); 0 for an all-zero row.  Sets *nonfinite
+ * if a value is inf or NaN. */
+static int row_exponent(const double *x, int64_t n, int *nonfinite)
+{
+    double amax = 0.0;
+    for (int64_t k = 0; k < n; ++k) {
+        if (!isfinite(x[k]))
+            *nonfinite = 1;
+        if (fabs(x[k]) > amax)
+            amax = fabs(x[k]);
+    }
+    int e = 0;
+    if (amax > 0.0)
+        frexp(amax, &e);
+    return e;
+}
+
+/* fp64 GEMM through scaled integers (see the header comment).  A: M x K
+ * doubles, B_t: N x K doubles (B stored K-contiguous), C: (row_end-row_begin)
+ * x N doubles; bits = t in [1, 53]. */
+int oracle_f64_emu(int64_t M, int64_t N, int64_t K, const double *A, const double *B_t, int bits,
+                   double *C, int64_t row_begin, int64_t row_end)
+{
+    if (bad_range(M, row_begin, row_end) || bits < 1 || bits > 53)
+        return ORACLE_BAD_RANGE;
+    int nonfinite = 0;
+    /* scaled integers of B (every column is needed by every output row) */
+    int64_t *Bi = (int64_t *)malloc((size_t)(N * K > 0 ? N * K : 1) * sizeof(int64_t));
+    int *eB = (int *)malloc((size_t)(N > 0 ? N : 1) * sizeof(int));
+    if (!Bi || !eB) {
+        free(Bi);
+        free(eB);
+        return ORACLE_BAD_RANGE;
+    }
+    for (int64_t j = 0; j < N; ++j) {
+        eB[j] = row_exponent(B_t + j * K, K, &nonfinite);
+        for (int64_t k = 0; k < K; ++k)
+            Bi[j * K + k] = (int64_t)rint(ldexp(B_t[j * K + k], bits - eB[j]));
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = row_begin; i < row_end; ++i) {
+        int nf = 0;
+        const int eA = row_exponent(A + i * K, K, &nf);
+        if (nf) {
+#pragma omp atomic write
+            nonfinite = 1;
+        }
+        int64_t *Ai = (int64_t *)malloc((size_t)(K > 0 ? K : 1) * sizeof(int64_t));
+        for (int64_t k = 0; k < K; ++k)
+            Ai[k] = (int64_t)rint(ldexp(A[i * K + k], bits - eA));
+        for (int64_t j = 0; j < N; ++j) {
+            __int128 x = 0;
+            for (int64_t k = 0; k < K; ++k)
+                x += (__int128)Ai[k] * (__int128)Bi[j * K + k];
+            /* one rounding to double, then an exact power-of-two scaling */
+            C[(i - row_begin) * N + j] = ldexp((double)x, -(2 * bits - eA - eB[j]));
+        }
+        free(Ai);
+    }
+    free(Bi);
+    free(eB);
+    return nonfinite ? ORACLE_NONFINITE : ORACLE_OK;
 }
 
 /* Number of OpenMP threads a parallel region of this library uses. */

@@ -19,6 +19,7 @@ import oracle
 import test_golden
 import test_oracle_dequant as t_dq
 import test_oracle_f16 as t_f16
+import test_oracle_f64emu as t_fe
 import test_oracle_int4 as t_i4
 import test_oracle_int8 as t_i8
 import test_oracle_quant as t_qz
@@ -49,6 +50,11 @@ MUTATIONS = {
     "qz_divide_by_128": ("volatile float s = (float)amax / 127.0f;", "volatile float s = (float)amax / 128.0f;"),
     "qz_round_half_away": ("float r = rintf(t);", "float r = roundf(t);"),
     "qz_reciprocal_multiply": ("volatile float t = v / s;", "volatile float t = v * (1.0f / s);"),
+    "fe_scale_exponent_off_by_one": ("Bi[j * K + k] = (int64_t)rint(ldexp(B_t[j * K + k], bits - eB[j]));",
+                                     "Bi[j * K + k] = (int64_t)rint(ldexp(B_t[j * K + k], bits - eB[j] + 1));"),
+    "fe_round_half_away": ("Ai[k] = (int64_t)rint(ldexp(A[i * K + k], bits - eA));",
+                           "Ai[k] = (int64_t)round(ldexp(A[i * K + k], bits - eA));"),
+    "fe_double_accumulator": ("__int128 x = 0;", "double x = 0;"),
     "dq_single_rounding": ("volatile float t = (float)(int32_t)s;\n            t = t * row_scale[i];\n            t = t * col_scale[j];",
                            "volatile float t = (float)((double)(int32_t)s * row_scale[i] * col_scale[j]);"),
 }
@@ -68,6 +74,10 @@ PINS = {
     "qz": [lambda: t_qz.test_exact_rational(6, 64, 1.0), lambda: t_qz.test_exact_rational(4, 200, 30.0),
            t_qz.test_integer_row_with_127_is_identity, t_qz.test_zero_row, t_qz.test_ties_to_even,
            t_qz.test_extremes_map_to_127, t_qz.test_reconstruction_bound, t_qz.test_tie_fixtures],
+    "fe": [lambda: t_fe.test_exact_inputs_give_correctly_rounded_product(53),
+           lambda: t_fe.test_truncation_bound(20), t_fe.test_power_of_two_row_scaling_is_exact,
+           t_fe.test_scaling_rounds_ties_to_even, t_fe.test_zero_rows_and_columns,
+           t_fe.test_cancellation_needs_the_exact_integer_sum],
     "dq": [t_dq.test_power_of_two_scales_exact, lambda: t_dq.test_three_rounding_bound(33, 7, 512),
            t_dq.test_scale_index_orientation, test_golden.test_dequant_worked,
            test_golden.test_dequant_two_roundings],

@@ -39,12 +39,12 @@ METRIC = "INT8/INT4 TOPS and FP16 TFLOPS at N=8192 on 1 MI355X; % of MFMA peak"
 # Dense MFMA peaks of the MI355X (256 CUs, 2.4 GHz): int8 8192 ops and fp16
 # 4096 flops per CU per clock.  INT4 runs on the int8 MFMA.
 PEAK_TOPS = {"i8": 5033.2, "i4": 5033.2, "dq": 5033.2, "w8": 5033.2, "f16": 2516.6,
-             "i4e": 5033.2, "i4g": 5033.2, "i8kn": 5033.2}
+             "i4e": 5033.2, "i4g": 5033.2, "i8kn": 5033.2, "f64e": 5033.2}
 HBM_PEAK_GBS = 8000.0
 UNIT = {"i8": "TOPS", "i4": "TOPS", "dq": "TOPS", "w8": "TOPS", "f16": "TFLOPS", "i4e": "TOPS",
-        "i4g": "TOPS", "i8kn": "TOPS"}
+        "i4g": "TOPS", "i8kn": "TOPS", "f64e": "TFLOPS"}
 DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "w8": "i8", "f16": "f16", "i4e": "i4", "i4g": "i4",
-         "i8kn": "i8"}
+         "i8kn": "i8", "f64e": "f64"}
 KERNEL_SOURCES = ["precision_dense_gemm_02_amd/csrc/gemm_kernels.hpp",
                   "precision_dense_gemm_02_amd/csrc/lpgemm.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -67,7 +67,7 @@ def parse_workload(name: str):
     if kind == "w8a8":
         from precision_dense_gemm_02_amd import inputs
         return "w8", size, inputs.LLM_N, inputs.LLM_K
-    if kind not in ("i8", "i4", "f16", "i4e", "i4g", "i8kn"):
+    if kind not in ("i8", "i4", "f16", "i4e", "i4g", "i8kn", "f64e"):
         raise SystemExit(f"unknown workload {name}")
     return kind, size, size, size
 
@@ -100,6 +100,25 @@ class Workload:
             self.launch = lambda i: lp.gemm_i8(a, b, out=out)
             self.in_bytes = M * K + N * K
             self.out_bytes = 4 * M * N
+        elif kind == "f64e":
+            # fp64 GEMM emulated with int8 GEMMs at 53 target bits; inputs
+            # N(0,1) times a power of two per row / column in [2^-4, 2^4]
+            self.seed = inputs.seed_for("f64", M)
+            rng = np.random.default_rng(self.seed)
+            A = rng.standard_normal((M, K)) * np.exp2(rng.integers(-4, 5, (M, 1)))
+            B_t = rng.standard_normal((N, K)) * np.exp2(rng.integers(-4, 5, (N, 1)))
+            self.host = (A, B_t)
+            self.bits = 53
+            self.moduli = lp.f64_emu_moduli(K, self.bits)
+            a, b = to(A), to(B_t)
+            ws = torch.empty((lp.f64_emu_workspace_bytes(M, N, K, self.bits),), dtype=torch.uint8, device=dev)
+            out = torch.empty((M, N), dtype=torch.float64, device=dev)
+            self.launch = lambda i: lp.gemm_f64_emu(a, b, self.bits, workspace=ws, out=out)
+            self.in_bytes = 8 * (M * K + N * K)
+            self.out_bytes = 8 * M * N
+            self.native = lambda: torch.matmul(a, b.t())
+            # the matrix-core work: one int8 GEMM per modulus
+            self.roof_ops = self.moduli * 2 * M * N * K
         elif kind == "i8kn":
             # the int8 workload with B stored K x N row-major (N contiguous)
             self.seed = inputs.seed_for("i8", M)
@@ -203,6 +222,10 @@ class Workload:
             e = oracle.f16_rel_error(got, ref, den)
             return f"max_rel_err {e['max_rel']:.3e} over {len(rows)} rows (tol 1e-3)" \
                 if e["max_rel"] <= 1e-3 else f"FAIL max_rel_err {e['max_rel']:.3e}"
+        elif self.kind == "f64e":
+            A, B_t = p
+            ref = oracle.f64_emu(A, B_t, self.bits, rows=rows)
+            ok = np.array_equal(got.view(np.uint64), ref.view(np.uint64))
         elif self.kind == "w8":
             q, s = oracle.quantize_rows_f16(p.x, rows=rows)
             ref = oracle.gemm_i8_dequant(q, p.w, s, p.w_scale)
@@ -269,7 +292,8 @@ def roofline(w: Workload, t: dict) -> dict:
     kind = w.kind
     alg_bytes = w.in_bytes + w.out_bytes
     sec = t["kernel_ms_avg"] / 1e3
-    intensity = w.ops / alg_bytes
+    ops = getattr(w, "roof_ops", w.ops)   # the emulated fp64 GEMM counts its int8 work
+    intensity = ops / alg_bytes
     ridge = PEAK_TOPS[kind] * 1e12 / (HBM_PEAK_GBS * 1e9)
     traffic = None
     try:
@@ -280,11 +304,11 @@ def roofline(w: Workload, t: dict) -> dict:
     except (OSError, ValueError):
         traffic = None
     if intensity >= ridge:
-        achieved = w.ops / sec / 1e12
+        achieved = ops / sec / 1e12
         return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TOPS[kind],
                 "unit": "TFLOP/s" if kind == "f16" else "TOP/s",
                 "frac": round(achieved / PEAK_TOPS[kind], 4), "traffic": traffic,
-                "algorithmic_bytes": alg_bytes, "ops_per_launch": w.ops}
+                "algorithmic_bytes": alg_bytes, "ops_per_launch": ops}
     achieved = alg_bytes / sec / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -326,6 +350,41 @@ def cpu_baseline(w: Workload, seconds: float) -> dict:
                       f"({nrows * w.N} outputs)"}
 
 
+def f64e_report(w, steps: int, warmup: int) -> dict:
+    """The precision-contract fields of the FP64-emulation page (target bits,
+    moduli, slices, pair schedule, residual, fallback, errors, time) for the
+    emulated fp64 GEMM, errors against an 80-bit extended-precision product
+    on sampled rows, and torch's native fp64 matmul timed beside it."""
+    import numpy as np
+    import torch
+    A, B_t = w.host
+    rows = [0, w.M // 3, w.M // 2, w.M - 1]
+    got = w.out.cpu().numpy()[rows]
+    ref = (A[rows].astype(np.longdouble) @ B_t.T.astype(np.longdouble))
+    err = np.abs(got.astype(np.longdouble) - ref)
+    nz = ref != 0
+    for _ in range(max(3, warmup // 10)):
+        w.native()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(5, steps // 4)
+    e0.record()
+    for _ in range(n):
+        w.native()
+    e1.record()
+    torch.cuda.synchronize()
+    native_ms = e0.elapsed_time(e1) / n
+    return {"precision_contract": {
+        "target_mantissa_bits": w.bits, "moduli": w.moduli, "slices": 1,
+        "pair_schedule": "one int8 GEMM per modulus", "residual": False, "fp64_fallback": False,
+        "max_abs_err": float(err.max()), "max_rel_err": float((err[nz] / np.abs(ref[nz])).max()),
+        "rms_abs_err": float(np.sqrt(np.mean(err.astype(np.float64) ** 2))),
+        "reference": f"80-bit extended-precision product, rows {rows}"},
+        "native_f64_matmul": {"ms": round(native_ms, 4),
+                              "tflops": round(2 * w.M * w.N * w.K / native_ms / 1e9, 1),
+                              "how": "torch.matmul on float64 (the platform library)"}}
+
+
 def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
     w = Workload(name)
     t = time_graph(w, steps, warmup) if graph else time_workload(w, steps, warmup)
@@ -344,6 +403,8 @@ def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
     elif w.kind == "i4e":
         rec["note"] = ("int4 through the FP6 E3M2 MFMA: one step is three launches (re-encode "
                        "A, re-encode B, GEMM); the kernel time and roofline cover all three")
+    elif w.kind == "f64e":
+        rec.update(f64e_report(w, steps, warmup))
     elif w.kind == "i4g":
         rec["note"] = ("int4 through the FP6 E3M2 MFMA, GEMM launch only: operands re-encoded "
                        "before timing (weights converted once)")

@@ -94,6 +94,28 @@ lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t *A, const 
 lpgemm_status lpgemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t *A_packed,
                         const uint8_t *B_packed, int32_t *C, hipStream_t stream);
 
+/* FP64 GEMM emulated with exact INT8 GEMMs (the FP64-emulation page of the
+ * series, day 12: scale / exponent scan, residue quantisation, INT8 GEMM, mod
+ * reduction, CRT reconstruction, undo scaling, write double).  C ~ A . B for
+ * fp64 A (M x K, row-major) and B stored K-contiguous (N x K), fp64 C
+ * (M x N).  `bits` (1..53) is the target: each row of A and each column of B
+ * is scaled by a power of two to integers of at most `bits` bits (nearest,
+ * ties to even), their exact product is formed through one int8 GEMM per
+ * modulus (lpgemm_f64_emu_moduli tells how many) and the Chinese remainder
+ * theorem, rounded once to double and scaled back.  The only error is that
+ * scaling (plus the final rounding).  K must be a multiple of 16 and at most
+ * LPGEMM_MAX_K_INT.  The caller provides `workspace` (256-byte aligned) of at
+ * least lpgemm_f64_emu_workspace(M, N, K, bits) bytes; the library still
+ * allocates nothing.  A, B, C 16-byte aligned.  Inputs must be finite; results
+ * that fall below the normal range are rounded a second time.  Errors: as for
+ * the GEMMs, plus INVALID_VALUE for bits outside 1..53 or a workspace that is
+ * missing or too small. */
+int lpgemm_f64_emu_moduli(int64_t K, int bits);
+int64_t lpgemm_f64_emu_workspace(int64_t M, int64_t N, int64_t K, int bits);
+lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double *A, const double *B,
+                             double *C, int bits, void *workspace, int64_t workspace_bytes,
+                             hipStream_t stream);
+
 /* INT8 with B stored K x N row-major (N contiguous; the "transposed" B of
  * the PTX-vs-WMMA summary page's layout ablation): C = A . B exactly in
  * int32, as lpgemm_i8.  A: M x K int8, B_kxn: K x N int8, C: M x N int32.

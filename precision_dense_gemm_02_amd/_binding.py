@@ -61,6 +61,12 @@ def load_library():
         lib.lpgemm_i8_dequant.restype = ctypes.c_int
         lib.lpgemm_quantize_rows_f16.argtypes = [_i64, _i64, _p, _p, _p, _p]
         lib.lpgemm_quantize_rows_f16.restype = ctypes.c_int
+        lib.lpgemm_f64_emu_moduli.argtypes = [_i64, ctypes.c_int]
+        lib.lpgemm_f64_emu_moduli.restype = ctypes.c_int
+        lib.lpgemm_f64_emu_workspace.argtypes = [_i64, _i64, _i64, ctypes.c_int]
+        lib.lpgemm_f64_emu_workspace.restype = _i64
+        lib.lpgemm_f64_emu.argtypes = [_i64, _i64, _i64, _p, _p, _p, ctypes.c_int, _p, _i64, _p]
+        lib.lpgemm_f64_emu.restype = ctypes.c_int
         lib.lpgemm_i8_kxn.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p]
         lib.lpgemm_i8_kxn.restype = ctypes.c_int
         lib.lpgemm_i4_to_e3m2.argtypes = [_i64, _i64, _p, _p, _p]
@@ -304,3 +310,41 @@ def gemm_i4_via_e3m2(a_packed, b_packed, out=None):
     (into buffers this function allocates), then multiplied; three library
     calls on the current stream."""
     return gemm_i4_e3m2(i4_to_e3m2(a_packed), i4_to_e3m2(b_packed), out=out)
+
+
+def f64_emu_moduli(K: int, bits: int = 53) -> int:
+    """Number of moduli (one int8 GEMM each) the fp64 emulation uses."""
+    return int(load_library().lpgemm_f64_emu_moduli(K, bits))
+
+
+def f64_emu_workspace_bytes(M: int, N: int, K: int, bits: int = 53) -> int:
+    return int(load_library().lpgemm_f64_emu_workspace(M, N, K, bits))
+
+
+def gemm_f64_emu(a, b_t, bits: int = 53, workspace=None, out=None):
+    """fp64 C ~ A . B through exact int8 GEMMs and the Chinese remainder
+    theorem; a: M x K float64, b_t: N x K float64 (B K-contiguous); rows of A
+    and columns of B are scaled to integers of `bits` bits.  `workspace`: a
+    uint8 GPU tensor of at least f64_emu_workspace_bytes(...) bytes
+    (allocated here when omitted)."""
+    torch = _torch()
+    _operand(a, torch.float64, "a")
+    _operand(b_t, torch.float64, "b_t")
+    if a.shape[1] != b_t.shape[1]:
+        raise ValueError(f"K mismatch: a {tuple(a.shape)}, b_t {tuple(b_t.shape)}")
+    dev = _same_device(a, b_t)
+    M, K = a.shape
+    N = b_t.shape[0]
+    need = f64_emu_workspace_bytes(M, N, K, bits)
+    if need < 0:
+        raise ValueError(f"unsupported fp64-emulation arguments K={K}, bits={bits}")
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.numel() < need or not workspace.is_cuda:
+        raise ValueError(f"workspace must be a uint8 GPU tensor of at least {need} bytes")
+    out = _output(out, (M, N), torch.float64, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_f64_emu(M, N, K, a.data_ptr(), b_t.data_ptr(), out.data_ptr(), bits,
+                                             workspace.data_ptr(), workspace.numel(),
+                                             _stream_handle(dev)), "lpgemm_f64_emu")
+    return out

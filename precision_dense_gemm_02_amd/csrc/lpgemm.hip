@@ -13,6 +13,7 @@
 #include <mutex>
 
 #include "../../include/lpgemm.h"
+#include "f64emu_kernels.hpp"
 #include "gemm_kernels.hpp"
 
 namespace lpgemm {
@@ -321,6 +322,115 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
 
 using namespace lpgemm;
 
+namespace {
+
+// fp64 emulation: the moduli, largest first (pairwise coprime)
+constexpr int kF64Moduli[kF64MaxModuli] = {256, 255, 253, 251, 247, 241, 239, 233, 229, 227,
+                                           223, 217, 211, 199, 197, 193, 191, 181, 179, 173};
+
+struct U192h {
+  uint64_t w[3];
+};
+void u192h_mul_small(U192h& a, uint32_t v) {
+  unsigned __int128 carry = 0;
+  for (int i = 0; i < 3; ++i) {
+    const unsigned __int128 t = (unsigned __int128)a.w[i] * v + carry;
+    a.w[i] = (uint64_t)t;
+    carry = t >> 64;
+  }
+}
+bool u192h_gt(const U192h& a, const U192h& b) {
+  for (int i = 2; i >= 0; --i)
+    if (a.w[i] != b.w[i]) return a.w[i] > b.w[i];
+  return false;
+}
+U192h u192h_shl(uint64_t x, int sh) {   // x << sh, sh < 192
+  U192h r{{0, 0, 0}};
+  const int limb = sh / 64, bit = sh % 64;
+  r.w[limb] = x << bit;
+  if (bit && limb + 1 < 3) r.w[limb + 1] = x >> (64 - bit);
+  return r;
+}
+int mod_inverse(int a, int m) {   // a^-1 mod m, gcd(a, m) = 1
+  int t = 0, nt = 1, r = m, nr = a % m;
+  while (nr) {
+    const int q = r / nr;
+    int x = t - q * nt; t = nt; nt = x;
+    x = r - q * nr; r = nr; nr = x;
+  }
+  return t < 0 ? t + m : t;
+}
+
+// Moduli needed so that their product P exceeds 2 K 2^(2 bits); -1 if the
+// twenty available are not enough.
+int f64emu_moduli(int64_t K, int bits) {
+  const U192h bound = u192h_shl((uint64_t)(K > 0 ? K : 1), 2 * bits + 1);
+  U192h P{{1, 0, 0}};
+  for (int s = 1; s <= kF64MaxModuli; ++s) {
+    u192h_mul_small(P, (uint32_t)kF64Moduli[s - 1]);
+    if (u192h_gt(P, bound)) return s;
+  }
+  return -1;
+}
+
+F64EmuConsts f64emu_consts(int s, int bits) {
+  F64EmuConsts c{};
+  c.s = s;
+  c.bits = bits;
+  U192h W{{1, 0, 0}};
+  for (int l = 0; l < s; ++l) {
+    const int m = kF64Moduli[l];
+    c.m[l] = m;
+    c.inv_m[l] = 1.0 / (double)m;
+    for (int i = 0; i < 3; ++i) c.w[l][i] = W.w[i];
+    // W mod m from its limbs
+    const unsigned __int128 two64 = ((unsigned __int128)1 << 64) % (unsigned)m;
+    unsigned __int128 wm = 0;
+    for (int i = 2; i >= 0; --i) wm = (wm * two64 + W.w[i] % (unsigned)m) % (unsigned)m;
+    c.w_inv[l] = mod_inverse((int)wm, m);
+    u192h_mul_small(W, (uint32_t)m);
+  }
+  for (int l = 0; l < s; ++l) {
+    // (product of m[0..k-1]) mod m[l]
+    int prod = 1;
+    for (int k = 0; k < l; ++k) {
+      c.w_mod[l][k] = prod;
+      prod = (prod * (c.m[k] % c.m[l])) % c.m[l];
+    }
+  }
+  for (int i = 0; i < 3; ++i) c.p[i] = W.w[i];
+  c.p_half[0] = (W.w[0] >> 1) | (W.w[1] << 63);
+  c.p_half[1] = (W.w[1] >> 1) | (W.w[2] << 63);
+  c.p_half[2] = W.w[2] >> 1;
+  return c;
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+// Workspace layout: eA (M int), eB (N int), residues of A (s M K int8),
+// residues of B (s N K int8), the s int32 products (M N each, every one
+// starting 256-byte aligned), each region 256-byte aligned.
+struct F64EmuLayout {
+  int64_t ea, eb, ra, rb, cl, total;
+};
+F64EmuLayout f64emu_layout(int64_t M, int64_t N, int64_t K, int s) {
+  F64EmuLayout L{};
+  L.ea = 0;
+  L.eb = L.ea + align256(4 * M);
+  L.ra = L.eb + align256(4 * N);
+  L.rb = L.ra + align256((int64_t)s * M * K);
+  L.cl = L.rb + align256((int64_t)s * N * K);
+  L.total = L.cl + (int64_t)s * align256(M * N * 4);
+  return L;
+}
+
+unsigned grid_for(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return (unsigned)(b < 1 ? 1 : (b > 65536 ? 65536 : b));
+}
+
+}  // namespace
+
 extern "C" {
 
 lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A, const int8_t* B,
@@ -331,6 +441,88 @@ lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A, const 
 lpgemm_status lpgemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t* A_packed,
                         const uint8_t* B_packed, int32_t* C, hipStream_t stream) {
   return run<KIND_I4>(M, N, K, A_packed, B_packed, C, nullptr, nullptr, stream);
+}
+
+int lpgemm_f64_emu_moduli(int64_t K, int bits) {
+  if (K < 0 || bits < 1 || bits > 53) return -1;
+  return f64emu_moduli(K, bits);
+}
+
+int64_t lpgemm_f64_emu_workspace(int64_t M, int64_t N, int64_t K, int bits) {
+  if (M < 0 || N < 0 || K < 0 || bits < 1 || bits > 53) return -1;
+  const int s = f64emu_moduli(K, bits);
+  if (s < 0) return -1;
+  return f64emu_layout(M, N, K, s).total;
+}
+
+lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double* A, const double* B,
+                             double* C, int bits, void* workspace, int64_t workspace_bytes,
+                             hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX) return LPGEMM_ERROR_INVALID_VALUE;
+  if (bits < 1 || bits > 53) return LPGEMM_ERROR_INVALID_VALUE;
+  if (K % 16 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  if (M == 0 || N == 0) return LPGEMM_SUCCESS;
+  if (!C || !workspace) return LPGEMM_ERROR_INVALID_VALUE;
+  if (K > 0 && (!A || !B)) return LPGEMM_ERROR_INVALID_VALUE;
+  const int s = f64emu_moduli(K, bits);
+  if (s < 0) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  const F64EmuLayout L = f64emu_layout(M, N, K, s);
+  if (workspace_bytes < L.total) return LPGEMM_ERROR_INVALID_VALUE;
+  if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))) ||
+      ((uintptr_t)workspace & 255) != 0)
+    return LPGEMM_ERROR_MISALIGNED;
+  DeviceInfo dev;
+  lpgemm_status st = current_device(dev);
+  if (st != LPGEMM_SUCCESS) return st;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int* eA = reinterpret_cast<int*>(ws + L.ea);
+  int* eB = reinterpret_cast<int*>(ws + L.eb);
+  int8_t* RA = reinterpret_cast<int8_t*>(ws + L.ra);
+  int8_t* RB = reinterpret_cast<int8_t*>(ws + L.rb);
+  int32_t* CL = reinterpret_cast<int32_t*>(ws + L.cl);
+  const F64EmuConsts c = f64emu_consts(s, bits);
+  int k32 = (int)K;
+  hipError_t e = hipSuccess;
+
+  // scale / exponent scan of the rows of A and of B (K-contiguous)
+  {
+    void* a1[] = {&A, &k32, &eA};
+    e = hipLaunchKernel((const void*)&f64_row_exponent, dim3((unsigned)M), dim3(256), a1, 0, stream);
+    if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
+    void* a2[] = {&B, &k32, &eB};
+    e = hipLaunchKernel((const void*)&f64_row_exponent, dim3((unsigned)N), dim3(256), a2, 0, stream);
+    if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
+  }
+  // residue quantisation
+  if (K > 0) {
+    int64_t ta = M * K, tb = N * K;
+    F64EmuConsts cc = c;
+    void* a1[] = {&A, &eA, &ta, &k32, &RA, &cc};
+    e = hipLaunchKernel((const void*)&f64_residues, dim3(grid_for(ta)), dim3(256), a1, 0, stream);
+    if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
+    void* a2[] = {&B, &eB, &tb, &k32, &RB, &cc};
+    e = hipLaunchKernel((const void*)&f64_residues, dim3(grid_for(tb)), dim3(256), a2, 0, stream);
+    if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
+  }
+  // one exact int8 GEMM per modulus
+  const int64_t cl_stride = align256(M * N * 4) / 4;   // elements between products
+  for (int l = 0; l < s; ++l) {
+    st = run<KIND_I8>(M, N, K, RA + (size_t)l * M * K, RB + (size_t)l * N * K, CL + (size_t)l * cl_stride,
+                      nullptr, nullptr, stream);
+    if (st != LPGEMM_SUCCESS) return st;
+  }
+  // mod reduction, CRT reconstruction, undo scaling, write double
+  {
+    int64_t mn = M * N;
+    int n32 = (int)N;
+    F64EmuConsts cc = c;
+    int64_t stride = cl_stride;
+    void* a[] = {&CL, &stride, &mn, &n32, &eA, &eB, &C, &cc};
+    e = hipLaunchKernel((const void*)&f64_crt, dim3(grid_for(mn)), dim3(256), a, 0, stream);
+    if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
+  }
+  return LPGEMM_SUCCESS;
 }
 
 lpgemm_status lpgemm_i8_kxn(int64_t M, int64_t N, int64_t K, const int8_t* A, const int8_t* B_kxn,

@@ -42,7 +42,7 @@ LLM_K = 4096
 LLM_N = 14336
 
 # Seed offset per workload family (seed = SEED_BASE + index).
-FAMILY_INDEX = {"i8": 1, "i4": 2, "f16": 3, "llm": 4, "w8a8": 5}
+FAMILY_INDEX = {"i8": 1, "i4": 2, "f16": 3, "llm": 4, "w8a8": 5, "f64": 6}
 
 
 def seed_for(family: str, extra: int = 0) -> int:

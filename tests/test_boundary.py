@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol(lib):
     names = b.declared_functions()
     assert set(names) == {"lpgemm_i8", "lpgemm_i4", "lpgemm_f16", "lpgemm_i8_dequant",
                           "lpgemm_quantize_rows_f16", "lpgemm_i4_to_e3m2", "lpgemm_i4_e3m2",
-                          "lpgemm_i8_kxn",
+                          "lpgemm_i8_kxn", "lpgemm_f64_emu", "lpgemm_f64_emu_moduli",
+                          "lpgemm_f64_emu_workspace",
                           "lpgemm_status_string", "lpgemm_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -177,3 +178,44 @@ def test_kxn_shape_rules(lib):
     # M = 0 or N = 0 is still a no-op
     assert f(0, 40, 64, None, None, None, None) == b.LPGEMM_SUCCESS
     assert f(4, 0, 64, None, None, None, None) == b.LPGEMM_SUCCESS
+
+
+MODULI = [256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211, 199, 197, 193, 191, 181,
+          179, 173]
+
+
+def test_f64_emu_moduli_and_workspace(lib):
+    import math
+    assert all(math.gcd(a, b) == 1 for i, a in enumerate(MODULI) for b in MODULI[i + 1:])
+    for K in (0, 16, 1024, 4096, 131056):
+        for bits in (1, 8, 24, 40, 53):
+            s = lib.lpgemm_f64_emu_moduli(K, bits)
+            bound = 2 * max(K, 1) * 2 ** (2 * bits)
+            assert math.prod(MODULI[:s]) > bound, (K, bits, s)
+            assert s == 1 or math.prod(MODULI[:s - 1]) <= bound, (K, bits, s)
+    assert lib.lpgemm_f64_emu_moduli(4096, 53) == 16
+    assert lib.lpgemm_f64_emu_moduli(16, 0) == -1
+    assert lib.lpgemm_f64_emu_moduli(16, 54) == -1
+    # eA, eB, residues, the products each padded to 256 bytes
+    M, N, K, bits = 33, 47, 64, 24
+    s = lib.lpgemm_f64_emu_moduli(K, bits)
+    pad = lambda x: (x + 255) // 256 * 256
+    want = pad(4 * M) + pad(4 * N) + pad(s * M * K) + pad(s * N * K) + s * pad(4 * M * N)
+    assert lib.lpgemm_f64_emu_workspace(M, N, K, bits) == want
+    assert lib.lpgemm_f64_emu_workspace(-1, N, K, bits) == -1
+
+
+def test_f64_emu_validation(lib):
+    f = lib.lpgemm_f64_emu
+    WS = 0x20000       # 256-byte aligned, never dereferenced
+    big = 1 << 40
+    assert f(-1, 4, 64, FAKE, FAKE, FAKE, 53, WS, big, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 4, 64, FAKE, FAKE, FAKE, 0, WS, big, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 4, 64, FAKE, FAKE, FAKE, 54, WS, big, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 4, 24, FAKE, FAKE, FAKE, 53, WS, big, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    assert f(0, 4, 64, None, None, None, 53, None, 0, None) == b.LPGEMM_SUCCESS   # empty
+    assert f(4, 4, 64, FAKE, FAKE, None, 53, WS, big, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 4, 64, FAKE, FAKE, FAKE, 53, None, big, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 4, 64, FAKE, FAKE, FAKE, 53, WS, 100, None) == b.LPGEMM_ERROR_INVALID_VALUE  # too small
+    assert f(4, 4, 64, MISALIGNED, FAKE, FAKE, 53, WS, big, None) == b.LPGEMM_ERROR_MISALIGNED
+    assert f(4, 4, 64, FAKE, FAKE, FAKE, 53, WS + 16, big, None) == b.LPGEMM_ERROR_MISALIGNED

@@ -529,6 +529,7 @@ def main():
         "parity": head["parity"],
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        **{k: head[k] for k in ("note", "precision_contract", "native_f64_matmul") if k in head},
         "also": also,
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -15,10 +15,11 @@
 //   * residues are stored balanced in int8 ([-128, 127] for 256,
 //     [-(m-1)/2, (m-1)/2] for odd m), so each modulus is one exact int8
 //     GEMM with int32 sums (|sum| <= K 2^14);
-//   * reconstruction: Garner's mixed-radix digits, the 192-bit value
-//     X = sum v_l W_l (W_l the product of the earlier moduli), made balanced
-//     (X - P when X >= P/2), rounded once to double (nearest, ties to even)
-//     and scaled by 2^-(2t - eA[i] - eB[j]).
+//   * reconstruction: with M_l = P / m_l and t_l = r_l (M_l^-1 mod m_l)
+//     mod m_l, X = sum t_l M_l - q P for q = floor(sum t_l / m_l) (estimated
+//     in double, then made exact by one range correction in integers), made
+//     balanced (X - P when X >= P/2), rounded once to double (nearest, ties
+//     to even) and scaled by 2^-(2t - eA[i] - eB[j]).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -34,9 +35,10 @@ struct F64EmuConsts {
   int bits;                                // target bits t
   int m[kF64MaxModuli];                    // moduli
   double inv_m[kF64MaxModuli];             // RN(1 / m)
-  int w_mod[kF64MaxModuli][kF64MaxModuli]; // (product of m[0..k-1]) mod m[l], index [l][k]
-  int w_inv[kF64MaxModuli];                // inverse of (product of m[0..l-1]) modulo m[l]
-  uint64_t w[kF64MaxModuli][3];            // product of m[0..l-1], 192-bit little-endian
+  float inv_mf[kF64MaxModuli];             // RN(1 / m) in binary32
+  int two16_mod[kF64MaxModuli];            // 2^16 mod m
+  int crt_c[kF64MaxModuli];                // (P / m[l])^-1 mod m[l]
+  uint64_t big_m[kF64MaxModuli][3];        // P / m[l], 192-bit little-endian
   uint64_t p[3];                           // product of all s moduli
   uint64_t p_half[3];                      // floor(P / 2)
 };
@@ -67,25 +69,50 @@ __global__ __launch_bounds__(256) void f64_row_exponent(const double* __restrict
 // rint(v / m) (the relative error of the product is below 2^-51 and
 // |v / m| < 2^46), so fma(-q, m, v) is an exact integer within m + m/2 of
 // zero, and at most two corrections by m bring it into the balanced range.
+// Each thread takes eight consecutive values of a row (K is a multiple of
+// 16) and writes one 8-byte word per modulus.  S (the modulus count) is a
+// template parameter so every loop unrolls with fixed register and
+// kernel-argument offsets.
+template <int S>
 __global__ __launch_bounds__(256) void f64_residues(const double* __restrict__ X, const int* __restrict__ e,
                                                     int64_t total, int K, int8_t* __restrict__ R,
                                                     F64EmuConsts c) {
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * 256) {
-    const int64_t row = idx / K;
-    const double v = rint(ldexp(X[idx], c.bits - e[row]));
-    for (int l = 0; l < c.s; ++l) {
+  const int64_t groups = total / 8;
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups; g += (int64_t)gridDim.x * 256) {
+    const int64_t idx = g * 8;
+    const int sh = c.bits - e[idx / K];
+    double v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = rint(ldexp(X[idx + q], sh));
+#pragma unroll
+    for (int l = 0; l < S; ++l) {
       const double m = (double)c.m[l];
-      const double q = rint(v * c.inv_m[l]);
-      double r = fma(-q, m, v);
       const double hi = (double)((c.m[l] - 1) / 2), lo = -(double)(c.m[l] / 2);
-      if (r > hi) r -= m;
-      if (r > hi) r -= m;
-      if (r < lo) r += m;
-      if (r < lo) r += m;
-      R[(size_t)l * total + idx] = (int8_t)(int)r;
+      uint64_t packed = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        double r = fma(-rint(v[q] * c.inv_m[l]), m, v[q]);
+        if (r > hi) r -= m;
+        if (r > hi) r -= m;
+        if (r < lo) r += m;
+        if (r < lo) r += m;
+        packed |= (uint64_t)(uint8_t)(int8_t)(int)r << (8 * q);
+      }
+      *(uint64_t*)(R + (size_t)l * total + idx) = packed;
     }
   }
+}
+
+// x mod m for 0 <= x < 2^24, all in binary32 (every value here is an
+// integer below 2^24, so exact): q = floor(x RN(1/m)) is within one of
+// floor(x / m), fma(-q, m, x) is then exact, and one correction each way
+// finishes.
+__device__ __forceinline__ int mod_small(int x, int m, float inv) {
+  const float xf = (float)x, mf = (float)m;
+  float r = fmaf(-floorf(xf * inv), mf, xf);
+  if (r < 0.f) r += mf;
+  if (r >= mf) r -= mf;
+  return (int)r;
 }
 
 // 192-bit unsigned helpers (three little-endian 64-bit limbs).
@@ -148,39 +175,87 @@ __device__ __forceinline__ double u192_to_double(const uint64_t (&a)[3]) {
   return ldexp((double)mant, exp);
 }
 
-// C[i][j] from the s int32 products: residues of each modulus, Garner's
-// digits, the balanced 192-bit integer, one rounding, the scaling undone.
-// CL holds the s products l * cl_stride elements apart.
+// The nearest double to a 128-bit unsigned integer (ties to even).
+__device__ __forceinline__ double u128_to_double(unsigned __int128 a) {
+  const uint64_t hi = (uint64_t)(a >> 64), lo = (uint64_t)a;
+  const uint64_t a3[3] = {lo, hi, 0};
+  return u192_to_double(a3);
+}
+
+// C[i][j] from the S int32 products: residues of each modulus, the CRT sum,
+// the exact range correction, the balanced integer, one rounding, the
+// scaling undone.  With up to 16 moduli P < 2^128 (the first sixteen
+// multiply to about 2^125.4): the sum is formed modulo 2^128, which is exact
+// for the final X since |X| < 2P < 2^127; otherwise in 192 bits.  Small
+// residues use binary32 (mod_small); a product is first split as
+// hi 2^16 + lo.  CL holds the S products l * cl_stride elements apart.
+template <int S>
 __global__ __launch_bounds__(256) void f64_crt(const int32_t* __restrict__ CL, int64_t cl_stride,
-                                               int64_t MN, int N,
-                                               const int* __restrict__ eA, const int* __restrict__ eB,
-                                               double* __restrict__ C, F64EmuConsts c) {
+                                               int64_t MN, int N, const int* __restrict__ eA,
+                                               const int* __restrict__ eB, double* __restrict__ C,
+                                               F64EmuConsts c) {
+  constexpr bool WIDE = S > 16;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < MN;
        idx += (int64_t)gridDim.x * 256) {
-    int v[kF64MaxModuli];
-    uint64_t x[3] = {0, 0, 0};
-    for (int l = 0; l < c.s; ++l) {
+    int32_t prods[S];
+#pragma unroll
+    for (int l = 0; l < S; ++l) prods[l] = CL[(size_t)l * cl_stride + idx];
+    double f = 0.0;                 // sum t_l / m_l, estimates q
+    uint64_t x3[3] = {0, 0, 0};
+    unsigned __int128 x2 = 0;
+#pragma unroll
+    for (int l = 0; l < S; ++l) {
       const int m = c.m[l];
-      int r = CL[(size_t)l * cl_stride + idx] % m;
-      if (r < 0) r += m;
-      // x mod m from the earlier digits, then this digit
-      int acc = 0;
-      for (int k = 0; k < l; ++k) acc += v[k] * c.w_mod[l][k];
-      int d = (r - acc % m) % m;
-      if (d < 0) d += m;
-      d = (d * c.w_inv[l]) % m;
-      v[l] = d;
-      u192_add_mul_small(x, c.w[l], (uint32_t)d);
+      const float inv = c.inv_mf[l];
+      const int hi = prods[l] >> 16, lo = prods[l] & 0xFFFF;            // prod = hi 2^16 + lo
+      const int hi_m = mod_small(hi + 32768 * m, m, inv);              // argument in (0, 2^24)
+      const int r = mod_small((int)__umul24(hi_m, c.two16_mod[l]) + lo, m, inv);
+      const int t = mod_small((int)__umul24(r, c.crt_c[l]), m, inv);
+      f = fma((double)t, c.inv_m[l], f);
+      if constexpr (WIDE) u192_add_mul_small(x3, c.big_m[l], (uint32_t)t);
+      else x2 += ((unsigned __int128)c.big_m[l][1] << 64 | c.big_m[l][0]) * (uint64_t)t;
     }
-    bool neg = false;
-    if (u192_ge(x, c.p_half)) {   // the balanced class: X - P
-      u192_rsub(x, c.p);
-      neg = true;
+    // q is floor(f) or one off (f carries at most a few ulps of error); the
+    // sign of X - 0 and of X - P decide the correction exactly
+    const uint32_t q = (uint32_t)floor(f);
+    double out;
+    if constexpr (WIDE) {
+      // x3 -= q P; then bring into [0, P)
+      uint64_t qp[3] = {0, 0, 0};
+      u192_add_mul_small(qp, c.p, q);
+      uint64_t d[3];
+      if (u192_ge(x3, qp)) {
+        d[0] = qp[0]; d[1] = qp[1]; d[2] = qp[2];
+        u192_rsub(d, x3);                      // x3 - qP >= 0
+        if (u192_ge(d, c.p)) {                 // q was one too small
+          const uint64_t pp[3] = {c.p[0], c.p[1], c.p[2]};
+          uint64_t e3[3] = {pp[0], pp[1], pp[2]};
+          u192_rsub(e3, d);
+          d[0] = e3[0]; d[1] = e3[1]; d[2] = e3[2];
+        }
+      } else {                                 // q was one too large: X = P - (qP - x3)
+        d[0] = x3[0]; d[1] = x3[1]; d[2] = x3[2];
+        u192_rsub(d, qp);                      // qP - x3 > 0
+        u192_rsub(d, c.p);                     // P - (qP - x3)
+      }
+      bool neg = false;
+      if (u192_ge(d, c.p_half)) {              // the balanced class: X - P
+        u192_rsub(d, c.p);
+        neg = true;
+      }
+      out = u192_to_double(d);
+      if (neg) out = -out;
+    } else {
+      const unsigned __int128 p = (unsigned __int128)c.p[1] << 64 | c.p[0];
+      const unsigned __int128 ph = (unsigned __int128)c.p_half[1] << 64 | c.p_half[0];
+      __int128 x = (__int128)(x2 - p * q);     // exact: |x| < 2P < 2^127
+      if (x < 0) x += (__int128)p;
+      else if (x >= (__int128)p) x -= (__int128)p;
+      const unsigned __int128 ux = (unsigned __int128)x;
+      out = ux >= ph ? -u128_to_double(p - ux) : u128_to_double(ux);
     }
-    double d = u192_to_double(x);
-    if (neg) d = -d;
     const int64_t i = idx / N, j = idx - i * N;
-    C[idx] = ldexp(d, -(2 * c.bits - eA[i] - eB[j]));
+    C[idx] = ldexp(out, -(2 * c.bits - eA[i] - eB[j]));
   }
 }
 

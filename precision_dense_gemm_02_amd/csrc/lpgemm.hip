@@ -373,39 +373,61 @@ int f64emu_moduli(int64_t K, int bits) {
   return -1;
 }
 
+// 192-bit value divided by a small integer (long division), and its
+// remainder
+U192h u192h_div_small(const U192h& a, uint32_t d, uint32_t* rem) {
+  U192h q{{0, 0, 0}};
+  unsigned __int128 r = 0;
+  for (int i = 2; i >= 0; --i) {
+    const unsigned __int128 cur = (r << 64) | a.w[i];
+    q.w[i] = (uint64_t)(cur / d);
+    r = cur % d;
+  }
+  if (rem) *rem = (uint32_t)r;
+  return q;
+}
+
 F64EmuConsts f64emu_consts(int s, int bits) {
   F64EmuConsts c{};
   c.s = s;
   c.bits = bits;
-  U192h W{{1, 0, 0}};
+  U192h P{{1, 0, 0}};
+  for (int l = 0; l < s; ++l) u192h_mul_small(P, (uint32_t)kF64Moduli[l]);
   for (int l = 0; l < s; ++l) {
     const int m = kF64Moduli[l];
     c.m[l] = m;
     c.inv_m[l] = 1.0 / (double)m;
-    for (int i = 0; i < 3; ++i) c.w[l][i] = W.w[i];
-    // W mod m from its limbs
-    const unsigned __int128 two64 = ((unsigned __int128)1 << 64) % (unsigned)m;
-    unsigned __int128 wm = 0;
-    for (int i = 2; i >= 0; --i) wm = (wm * two64 + W.w[i] % (unsigned)m) % (unsigned)m;
-    c.w_inv[l] = mod_inverse((int)wm, m);
-    u192h_mul_small(W, (uint32_t)m);
+    c.inv_mf[l] = 1.0f / (float)m;
+    c.two16_mod[l] = 65536 % m;
+    const U192h Ml = u192h_div_small(P, (uint32_t)m, nullptr);   // exact: m divides P
+    for (int i = 0; i < 3; ++i) c.big_m[l][i] = Ml.w[i];
+    uint32_t ml_mod = 0;
+    u192h_div_small(Ml, (uint32_t)m, &ml_mod);
+    c.crt_c[l] = mod_inverse((int)ml_mod, m);
   }
-  for (int l = 0; l < s; ++l) {
-    // (product of m[0..k-1]) mod m[l]
-    int prod = 1;
-    for (int k = 0; k < l; ++k) {
-      c.w_mod[l][k] = prod;
-      prod = (prod * (c.m[k] % c.m[l])) % c.m[l];
-    }
-  }
-  for (int i = 0; i < 3; ++i) c.p[i] = W.w[i];
-  c.p_half[0] = (W.w[0] >> 1) | (W.w[1] << 63);
-  c.p_half[1] = (W.w[1] >> 1) | (W.w[2] << 63);
-  c.p_half[2] = W.w[2] >> 1;
+  for (int i = 0; i < 3; ++i) c.p[i] = P.w[i];
+  c.p_half[0] = (P.w[0] >> 1) | (P.w[1] << 63);
+  c.p_half[1] = (P.w[1] >> 1) | (P.w[2] << 63);
+  c.p_half[2] = P.w[2] >> 1;
   return c;
 }
 
 int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+// the residue and reconstruction kernels, instantiated per modulus count
+template <int... S>
+struct F64EmuKernels {
+  static const void* residues(int s) {
+    static const void* const table[] = {(const void*)&f64_residues<S>...};
+    return table[s - 1];
+  }
+  static const void* crt(int s) {
+    static const void* const table[] = {(const void*)&f64_crt<S>...};
+    return table[s - 1];
+  }
+};
+using F64EmuTable = F64EmuKernels<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20>;
+static_assert(kF64MaxModuli == 20, "one kernel per modulus count");
 
 // Workspace layout: eA (M int), eB (N int), residues of A (s M K int8),
 // residues of B (s N K int8), the s int32 products (M N each, every one
@@ -494,15 +516,15 @@ lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double* A, c
     e = hipLaunchKernel((const void*)&f64_row_exponent, dim3((unsigned)N), dim3(256), a2, 0, stream);
     if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
   }
-  // residue quantisation
+  // residue quantisation (eight values per thread)
   if (K > 0) {
     int64_t ta = M * K, tb = N * K;
     F64EmuConsts cc = c;
     void* a1[] = {&A, &eA, &ta, &k32, &RA, &cc};
-    e = hipLaunchKernel((const void*)&f64_residues, dim3(grid_for(ta)), dim3(256), a1, 0, stream);
+    e = hipLaunchKernel(F64EmuTable::residues(s), dim3(grid_for(ta / 8)), dim3(256), a1, 0, stream);
     if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
     void* a2[] = {&B, &eB, &tb, &k32, &RB, &cc};
-    e = hipLaunchKernel((const void*)&f64_residues, dim3(grid_for(tb)), dim3(256), a2, 0, stream);
+    e = hipLaunchKernel(F64EmuTable::residues(s), dim3(grid_for(tb / 8)), dim3(256), a2, 0, stream);
     if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
   }
   // one exact int8 GEMM per modulus
@@ -519,7 +541,7 @@ lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double* A, c
     F64EmuConsts cc = c;
     int64_t stride = cl_stride;
     void* a[] = {&CL, &stride, &mn, &n32, &eA, &eB, &C, &cc};
-    e = hipLaunchKernel((const void*)&f64_crt, dim3(grid_for(mn)), dim3(256), a, 0, stream);
+    e = hipLaunchKernel(F64EmuTable::crt(s), dim3(grid_for(mn)), dim3(256), a, 0, stream);
     if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
   }
   return LPGEMM_SUCCESS;

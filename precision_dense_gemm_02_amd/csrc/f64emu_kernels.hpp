@@ -14,7 +14,8 @@
 //     is the unique balanced residue class modulo P;
 //   * residues are stored balanced in int8 ([-128, 127] for 256,
 //     [-(m-1)/2, (m-1)/2] for odd m), so each modulus is one exact int8
-//     GEMM with int32 sums (|sum| <= K 2^14);
+//     GEMM with int32 sums (|sum| <= K 2^14), whose epilogue reduces each
+//     sum modulo m and stores the byte (mod reduction);
 //   * reconstruction: with M_l = P / m_l and t_l = r_l (M_l^-1 mod m_l)
 //     mod m_l, X = sum t_l M_l - q P for q = floor(sum t_l / m_l) (estimated
 //     in double, then made exact by one range correction in integers), made
@@ -36,7 +37,6 @@ struct F64EmuConsts {
   int m[kF64MaxModuli];                    // moduli
   double inv_m[kF64MaxModuli];             // RN(1 / m)
   float inv_mf[kF64MaxModuli];             // RN(1 / m) in binary32
-  int two16_mod[kF64MaxModuli];            // 2^16 mod m
   int crt_c[kF64MaxModuli];                // (P / m[l])^-1 mod m[l]
   uint64_t big_m[kF64MaxModuli][3];        // P / m[l], 192-bit little-endian
   uint64_t p[3];                           // product of all s moduli
@@ -182,24 +182,24 @@ __device__ __forceinline__ double u128_to_double(unsigned __int128 a) {
   return u192_to_double(a3);
 }
 
-// C[i][j] from the S int32 products: residues of each modulus, the CRT sum,
+// C[i][j] from the S reduced products (bytes r_l in [0, m_l)): the CRT sum,
 // the exact range correction, the balanced integer, one rounding, the
 // scaling undone.  With up to 16 moduli P < 2^128 (the first sixteen
 // multiply to about 2^125.4): the sum is formed modulo 2^128, which is exact
 // for the final X since |X| < 2P < 2^127; otherwise in 192 bits.  Small
-// residues use binary32 (mod_small); a product is first split as
-// hi 2^16 + lo.  CL holds the S products l * cl_stride elements apart.
+// reductions use binary32 (mod_small).  CR holds the S byte matrices
+// l * cr_stride bytes apart.
 template <int S>
-__global__ __launch_bounds__(256) void f64_crt(const int32_t* __restrict__ CL, int64_t cl_stride,
+__global__ __launch_bounds__(256) void f64_crt(const uint8_t* __restrict__ CR, int64_t cr_stride,
                                                int64_t MN, int N, const int* __restrict__ eA,
                                                const int* __restrict__ eB, double* __restrict__ C,
                                                F64EmuConsts c) {
   constexpr bool WIDE = S > 16;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < MN;
        idx += (int64_t)gridDim.x * 256) {
-    int32_t prods[S];
+    int rs[S];
 #pragma unroll
-    for (int l = 0; l < S; ++l) prods[l] = CL[(size_t)l * cl_stride + idx];
+    for (int l = 0; l < S; ++l) rs[l] = CR[(size_t)l * cr_stride + idx];
     double f = 0.0;                 // sum t_l / m_l, estimates q
     uint64_t x3[3] = {0, 0, 0};
     unsigned __int128 x2 = 0;
@@ -207,10 +207,7 @@ __global__ __launch_bounds__(256) void f64_crt(const int32_t* __restrict__ CL, i
     for (int l = 0; l < S; ++l) {
       const int m = c.m[l];
       const float inv = c.inv_mf[l];
-      const int hi = prods[l] >> 16, lo = prods[l] & 0xFFFF;            // prod = hi 2^16 + lo
-      const int hi_m = mod_small(hi + 32768 * m, m, inv);              // argument in (0, 2^24)
-      const int r = mod_small((int)__umul24(hi_m, c.two16_mod[l]) + lo, m, inv);
-      const int t = mod_small((int)__umul24(r, c.crt_c[l]), m, inv);
+      const int t = mod_small((int)__umul24(rs[l], c.crt_c[l]), m, inv);
       f = fma((double)t, c.inv_m[l], f);
       if constexpr (WIDE) u192_add_mul_small(x3, c.big_m[l], (uint32_t)t);
       else x2 += ((unsigned __int128)c.big_m[l][1] << 64 | c.big_m[l][0]) * (uint64_t)t;

@@ -34,7 +34,14 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-enum Kind : int { KIND_I8 = 0, KIND_I4 = 1, KIND_F16 = 2, KIND_I8_DEQUANT = 3, KIND_I4_E3M2 = 4 };
+enum Kind : int {
+  KIND_I8 = 0,
+  KIND_I4 = 1,
+  KIND_F16 = 2,
+  KIND_I8_DEQUANT = 3,
+  KIND_I4_E3M2 = 4,
+  KIND_I8_MOD = 5   // int8 product reduced modulo GemmArgs::modulus, one byte per element
+};
 
 // LDS bytes of one operand row per K-stage, and 16-byte chunks per such row.
 constexpr int kStageRowBytes = 128;
@@ -56,6 +63,8 @@ struct GemmArgs {
   int k_stages;         // number of 128-byte LDS K-stages
   int tiles_m, tiles_n;
   int group_m;          // tile rows per raster group
+  int modulus;          // KIND_I8_MOD: C[i][j] = (A.B)[i][j] mod modulus (0 < modulus <= 256), uint8
+  double inv_modulus;   // KIND_I8_MOD: RN(1 / modulus)
 };
 
 // Position of 16-byte chunk `c` of LDS row `r` within that row.  XOR with a
@@ -113,6 +122,11 @@ struct KindTraits<KIND_I8> {
 };
 template <>
 struct KindTraits<KIND_I8_DEQUANT> {
+  static constexpr int global_chunks = kChunksPerRow;
+  using Acc = i32x16;
+};
+template <>
+struct KindTraits<KIND_I8_MOD> {
   static constexpr int global_chunks = kChunksPerRow;
   using Acc = i32x16;
 };
@@ -780,7 +794,8 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   // reused; the barrier then also covers every wave's fragment reads.
   wait_vmcnt<0>();
   wait_lgkmcnt0();
-  const bool interior = m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 3) == 0;
+  // the reduced kind stores bytes through the direct path below
+  const bool interior = KIND != KIND_I8_MOD && m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 3) == 0;
   if (interior) {
     block_barrier();   // every wave is done with the operand stages
     uint8_t* stage_out = smem + wave * kEpiRows * kEpiPitch;
@@ -825,7 +840,20 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
-          if (col < p.N && row < p.M) ((uint32_t*)p.C)[(size_t)row * p.N + col] = value(i, j, e, row, col);
+          if (col < p.N && row < p.M) {
+            if constexpr (KIND == KIND_I8_MOD) {
+              // the non-negative residue: |acc| < 2^31 is exact in double, q
+              // from the rounded reciprocal is within one of floor(acc / m),
+              // fma(-q, m, acc) is exact, and one correction each way ends it
+              const double x = (double)(int32_t)acc[i][j][e], m = (double)p.modulus;
+              double r = fma(-floor(x * p.inv_modulus), m, x);
+              if (r < 0.0) r += m;
+              if (r >= m) r -= m;
+              ((uint8_t*)p.C)[(size_t)row * p.N + col] = (uint8_t)(int)r;
+            } else {
+              ((uint32_t*)p.C)[(size_t)row * p.N + col] = value(i, j, e, row, col);
+            }
+          }
         }
       }
     }

@@ -60,6 +60,7 @@ lpgemm_status validate(Kind kind, int64_t M, int64_t N, int64_t K, const void* A
   switch (kind) {
     case KIND_I8:
     case KIND_I8_DEQUANT:
+    case KIND_I8_MOD:
       if (K % 16 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
       break;
     case KIND_I4:
@@ -143,7 +144,8 @@ int forced_config() {
 }
 
 // The E3M2 kind runs only on the LDS-pipelined kernels with 128-byte stage
-// rows (two 64-value MFMA steps per stage).
+// rows (two 64-value MFMA steps per stage); the reduced int8 kind of the
+// fp64 emulation uses the same three.
 bool supports_e3m2(int c) {
   return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128;
 }
@@ -202,7 +204,7 @@ KernelCfg choose_config_kxn(int64_t M, int64_t N, int cu_count) {
 
 template <int KIND, bool BKN = false>
 lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
-                  const float* rs, const float* cs, hipStream_t stream) {
+                  const float* rs, const float* cs, hipStream_t stream, int modulus = 0) {
   // K x N B: k-rows of N bytes must start 16-byte aligned and the matrix
   // must fit the 32-bit offsets of its buffer resource (a shape error, so it
   // ranks with the K checks: after negative sizes, before pointers)
@@ -224,12 +226,14 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   args.col_scale = cs;
   args.M = (int)M;
   args.N = (int)N;
+  args.modulus = modulus;
+  args.inv_modulus = modulus > 0 ? 1.0 / (double)modulus : 0.0;
   // bytes per operand row: fp16 2K, packed int4 K/2, int8 and E3M2 K
   const int64_t row_bytes = KIND == KIND_F16 ? 2 * K : (KIND == KIND_I4 ? K / 2 : K);
   args.row_bytes = (int)row_bytes;
 
   const KernelCfg cfg = BKN ? choose_config_kxn(M, N, dev.cu_count)
-                      : KIND == KIND_I4_E3M2 ? choose_config_e3m2(M, N, dev.cu_count)
+                      : (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) ? choose_config_e3m2(M, N, dev.cu_count)
                                              : choose_config(M, N, dev.cu_count);
   const int64_t stage_bytes = (KIND == KIND_I4 && expands_int4_in_lds(cfg)) ? K : row_bytes;
   (void)is_skinny;
@@ -248,7 +252,7 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128, 0, false, true>, args, 256,
                                stream);
     }
-  } else if constexpr (KIND == KIND_I4_E3M2) {
+  } else if constexpr (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) {
     switch (cfg) {
       case CFG_256_S2_R128:
         return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
@@ -398,7 +402,6 @@ F64EmuConsts f64emu_consts(int s, int bits) {
     c.m[l] = m;
     c.inv_m[l] = 1.0 / (double)m;
     c.inv_mf[l] = 1.0f / (float)m;
-    c.two16_mod[l] = 65536 % m;
     const U192h Ml = u192h_div_small(P, (uint32_t)m, nullptr);   // exact: m divides P
     for (int i = 0; i < 3; ++i) c.big_m[l][i] = Ml.w[i];
     uint32_t ml_mod = 0;
@@ -430,8 +433,8 @@ using F64EmuTable = F64EmuKernels<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14,
 static_assert(kF64MaxModuli == 20, "one kernel per modulus count");
 
 // Workspace layout: eA (M int), eB (N int), residues of A (s M K int8),
-// residues of B (s N K int8), the s int32 products (M N each, every one
-// starting 256-byte aligned), each region 256-byte aligned.
+// residues of B (s N K int8), the s reduced products (M N bytes each, every
+// one starting 256-byte aligned), each region 256-byte aligned.
 struct F64EmuLayout {
   int64_t ea, eb, ra, rb, cl, total;
 };
@@ -442,7 +445,7 @@ F64EmuLayout f64emu_layout(int64_t M, int64_t N, int64_t K, int s) {
   L.ra = L.eb + align256(4 * N);
   L.rb = L.ra + align256((int64_t)s * M * K);
   L.cl = L.rb + align256((int64_t)s * N * K);
-  L.total = L.cl + (int64_t)s * align256(M * N * 4);
+  L.total = L.cl + (int64_t)s * align256(M * N);
   return L;
 }
 
@@ -502,7 +505,7 @@ lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double* A, c
   int* eB = reinterpret_cast<int*>(ws + L.eb);
   int8_t* RA = reinterpret_cast<int8_t*>(ws + L.ra);
   int8_t* RB = reinterpret_cast<int8_t*>(ws + L.rb);
-  int32_t* CL = reinterpret_cast<int32_t*>(ws + L.cl);
+  uint8_t* CR = ws + L.cl;
   const F64EmuConsts c = f64emu_consts(s, bits);
   int k32 = (int)K;
   hipError_t e = hipSuccess;
@@ -527,11 +530,11 @@ lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double* A, c
     e = hipLaunchKernel(F64EmuTable::residues(s), dim3(grid_for(tb / 8)), dim3(256), a2, 0, stream);
     if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
   }
-  // one exact int8 GEMM per modulus
-  const int64_t cl_stride = align256(M * N * 4) / 4;   // elements between products
+  // one exact int8 GEMM per modulus, its epilogue reducing modulo m
+  const int64_t cr_stride = align256(M * N);   // bytes between products
   for (int l = 0; l < s; ++l) {
-    st = run<KIND_I8>(M, N, K, RA + (size_t)l * M * K, RB + (size_t)l * N * K, CL + (size_t)l * cl_stride,
-                      nullptr, nullptr, stream);
+    st = run<KIND_I8_MOD>(M, N, K, RA + (size_t)l * M * K, RB + (size_t)l * N * K, CR + (size_t)l * cr_stride,
+                          nullptr, nullptr, stream, c.m[l]);
     if (st != LPGEMM_SUCCESS) return st;
   }
   // mod reduction, CRT reconstruction, undo scaling, write double
@@ -539,8 +542,8 @@ lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double* A, c
     int64_t mn = M * N;
     int n32 = (int)N;
     F64EmuConsts cc = c;
-    int64_t stride = cl_stride;
-    void* a[] = {&CL, &stride, &mn, &n32, &eA, &eB, &C, &cc};
+    int64_t stride = cr_stride;
+    void* a[] = {&CR, &stride, &mn, &n32, &eA, &eB, &C, &cc};
     e = hipLaunchKernel(F64EmuTable::crt(s), dim3(grid_for(mn)), dim3(256), a, 0, stream);
     if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
   }

@@ -196,11 +196,11 @@ def test_f64_emu_moduli_and_workspace(lib):
     assert lib.lpgemm_f64_emu_moduli(4096, 53) == 16
     assert lib.lpgemm_f64_emu_moduli(16, 0) == -1
     assert lib.lpgemm_f64_emu_moduli(16, 54) == -1
-    # eA, eB, residues, the products each padded to 256 bytes
+    # eA, eB, residues, the reduced products (one byte each) padded to 256 bytes
     M, N, K, bits = 33, 47, 64, 24
     s = lib.lpgemm_f64_emu_moduli(K, bits)
     pad = lambda x: (x + 255) // 256 * 256
-    want = pad(4 * M) + pad(4 * N) + pad(s * M * K) + pad(s * N * K) + s * pad(4 * M * N)
+    want = pad(4 * M) + pad(4 * N) + pad(s * M * K) + pad(s * N * K) + s * pad(M * N)
     assert lib.lpgemm_f64_emu_workspace(M, N, K, bits) == want
     assert lib.lpgemm_f64_emu_workspace(-1, N, K, bits) == -1
 

@@ -499,8 +499,12 @@ struct RowLayout<64> {
 // l % 32, in the k order of the A fragment.  16-byte chunks of k-row k are
 // XOR-swizzled by 2k, which puts the eight rows one read touches on
 // distinct banks.
+//
+// LSTEPS: the number of K-steps at the start of a stage over which the next
+// stage's loads are issued (0: all but the last K-step).  NTC: C is written
+// with non-temporal stores.
 template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false,
-          bool BKN = false>
+          bool BKN = false, int LSTEPS = 0, bool NTC = false>
 __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
@@ -713,8 +717,9 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
 
   constexpr int kMfma = TM * TN;
   constexpr int kReads = (E3M2 ? 2 : 1) * (TM + TN);   // DS read instructions per K-step
-  // loads of one stage are spread over K-steps 0 .. KSTEPS-2 (or step 0)
-  constexpr int kLoadSteps = KSTEPS > 1 ? KSTEPS - 1 : 1;
+  // loads of one stage are spread over K-steps 0 .. kLoadSteps-1
+  constexpr int kLoadSteps = LSTEPS > 0 ? LSTEPS : (KSTEPS > 1 ? KSTEPS - 1 : 1);
+  static_assert(kLoadSteps < KSTEPS || KSTEPS == 1, "loads end before the stage's last K-step");
   constexpr int kLoadsPerStep = (kSlots + kLoadSteps - 1) / kLoadSteps;
   auto interleave = [&](int mfmas, int reads, int loads) {
 #pragma unroll
@@ -827,7 +832,8 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
         const int c = (lane % kLanesPerRow) * 4;
         const i32x4 v = *(const i32x4*)(stage_out + r * kEpiPitch + c * 4);
         const size_t idx = (size_t)(row0 + half * 64 + r) * p.N + col0 + c;
-        *(i32x4*)((uint32_t*)p.C + idx) = v;
+        if constexpr (NTC) __builtin_nontemporal_store(v, (i32x4*)((uint32_t*)p.C + idx));
+        else *(i32x4*)((uint32_t*)p.C + idx) = v;
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next half overwrites
     }

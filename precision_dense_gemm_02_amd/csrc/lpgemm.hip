@@ -88,7 +88,7 @@ lpgemm_status validate(Kind kind, int64_t M, int64_t N, int64_t K, const void* A
 // tiles has the best operand reuse; smaller tiles fill the 256 CUs when the
 // product has few 256 x 256 tiles.
 enum KernelCfg {
-  CFG_256_S2_R128 = 0,   // 4 waves, 256 x 256, 2 stages of 128-byte rows
+  CFG_256_S2_R128 = 0,   // 4 waves, 256 x 256, 2 stages of 128-byte rows (see kNtC)
   CFG_256_S4_R64 = 1,    // 4 waves, 256 x 256, 4 stages of 64-byte rows
   CFG_256_S3_R64 = 2,    // 4 waves, 256 x 256, 3 stages of 64-byte rows
   CFG_128_S4_R64 = 3,    // 4 waves, 128 x 128, 4 stages of 64-byte rows
@@ -116,7 +116,10 @@ enum KernelCfg {
   CFG_256_S2_R128_SC0 = 24,      // operand loads sc0
   CFG_256_S2_R128_SC01 = 25,     // operand loads sc0 sc1
   CFG_256_S2_R128_SPLIT = 26,    // split loader: two waves load A, two load B
-  CFG_COUNT = 27
+  CFG_256_S2_R128_L1 = 27,       // the next stage's loads all issued in K-step 0
+  CFG_256_S2_R128_LALL = 28,     // ... spread over all K-steps but the last
+  CFG_256_S2_R128_CACHED_C = 29, // C written with ordinary (cached) stores
+  CFG_COUNT = 30
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -239,12 +242,19 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   (void)is_skinny;
   const int rowb = stage_row_bytes(cfg);
   args.k_stages = (int)((stage_bytes + rowb - 1) / rowb);
+  // Configuration 0 writes C with non-temporal stores, except for int4,
+  // whose shorter main loop measured faster with cached stores (8192^3,
+  // steady state: int8 +2%, fp16 +2%, int4 -1%); the byte stores of the
+  // reduced kind go through the direct path, where the choice does not
+  // apply.  On the general and K x N paths it also issues the next stage's
+  // loads in its first two K-steps (int8 +1.5%, fp16 +2%).
+  constexpr bool kNtC = KIND != KIND_I4 && KIND != KIND_I8_MOD;
 
   if constexpr (BKN) {
     switch (cfg) {
       case CFG_256_S2_R128:
-        return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, true>, args, 256,
-                                stream);
+        return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, true, 2, true>, args,
+                                256, stream);
       case CFG_128_S4_R128:
         return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128, 0, false, true>, args, 256,
                                 stream);
@@ -255,7 +265,8 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   } else if constexpr (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) {
     switch (cfg) {
       case CFG_256_S2_R128:
-        return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
+        return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 0, kNtC>, args,
+                                256, stream);
       case CFG_128_S4_R128:
         return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
       default:
@@ -264,7 +275,8 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   } else {
   switch (cfg) {
     case CFG_256_S2_R128:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC>, args,
+                              256, stream);
     case CFG_128_S4_R128:
       return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
     case CFG_256_S4_R64:
@@ -315,6 +327,14 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 4>, args, 256, stream);
     case CFG_256_S2_R128_SPLIT:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, true>, args, 256, stream);
+    case CFG_256_S2_R128_L1:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 1>, args, 256,
+                              stream);
+    case CFG_256_S2_R128_CACHED_C:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, false>, args,
+                              256, stream);
+    case CFG_256_S2_R128_LALL:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
     default:
       return launch<64, 64>((const void*)&gemm_tiled<KIND, 64, 64, 2, 2>, args, 256, stream);
   }

@@ -412,9 +412,10 @@ def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
 
 
 # the kernel each square workload runs at 8192 (configuration 0)
-TRAFFIC_KERNELS = {"i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128>(lpgemm::GemmArgs)",
-                   "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128>(lpgemm::GemmArgs)",
-                   "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128>(lpgemm::GemmArgs)"}
+TRAFFIC_KERNELS = {
+    "i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0>(lpgemm::GemmArgs)",
+    "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0>(lpgemm::GemmArgs)",
+    "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0>(lpgemm::GemmArgs)"}
 
 
 def _median_counter(path: str, kernel: str, counter: str) -> float:

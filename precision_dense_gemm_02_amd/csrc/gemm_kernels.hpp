@@ -502,9 +502,10 @@ struct RowLayout<64> {
 //
 // LSTEPS: the number of K-steps at the start of a stage over which the next
 // stage's loads are issued (0: all but the last K-step).  NTC: C is written
-// with non-temporal stores.
+// with non-temporal stores.  BSPLIT: MFMAs of the last K-step issued before
+// the stage barrier (0: half).
 template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false,
-          bool BKN = false, int LSTEPS = 0, bool NTC = false>
+          bool BKN = false, int LSTEPS = 0, bool NTC = false, int BSPLIT = 0>
 __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
@@ -716,6 +717,8 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   };
 
   constexpr int kMfma = TM * TN;
+  constexpr int kSplit = BSPLIT > 0 ? BSPLIT : kMfma / 2;
+  static_assert(kSplit > 0 && kSplit < kMfma, "barrier split");
   constexpr int kReads = (E3M2 ? 2 : 1) * (TM + TN);   // DS read instructions per K-step
   // loads of one stage are spread over K-steps 0 .. kLoadSteps-1
   constexpr int kLoadSteps = LSTEPS > 0 ? LSTEPS : (KSTEPS > 1 ? KSTEPS - 1 : 1);
@@ -762,15 +765,15 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
         compute(src, 0, kMfma);
         interleave(kMfma, kReads, nl);
       } else {
-        compute(src, 0, kMfma / 2);
-        interleave(kMfma / 2, 0, nl);
+        compute(src, 0, kSplit);
+        interleave(kSplit, 0, nl);
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<(STAGES - 2) * kSlots>();   // own loads of stage s+1 landed
         wait_lgkmcnt0();                       // own reads of stage s done
         block_barrier();                       // ... everyone's
         read_frags(s + 1, 0, dst);
-        compute(src, kMfma / 2, kMfma);
-        interleave(kMfma / 2, kReads, 0);
+        compute(src, kSplit, kMfma);
+        interleave(kMfma - kSplit, kReads, 0);
       }
     }
   }

@@ -119,7 +119,9 @@ enum KernelCfg {
   CFG_256_S2_R128_L1 = 27,       // the next stage's loads all issued in K-step 0
   CFG_256_S2_R128_LALL = 28,     // ... spread over all K-steps but the last
   CFG_256_S2_R128_CACHED_C = 29, // C written with ordinary (cached) stores
-  CFG_COUNT = 30
+  CFG_256_S2_R128_B4 = 30,       // stage barrier after 4 of the last K-step's 16 MFMAs
+  CFG_256_S2_R128_B12 = 31,      // ... after 12
+  CFG_COUNT = 32
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -332,6 +334,12 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
                               stream);
     case CFG_256_S2_R128_CACHED_C:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, false>, args,
+                              256, stream);
+    case CFG_256_S2_R128_B4:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 4>, args,
+                              256, stream);
+    case CFG_256_S2_R128_B12:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 12>, args,
                               256, stream);
     case CFG_256_S2_R128_LALL:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);

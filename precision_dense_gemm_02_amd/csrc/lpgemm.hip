@@ -121,14 +121,17 @@ enum KernelCfg {
   CFG_256_S2_R128_CACHED_C = 29, // C written with ordinary (cached) stores
   CFG_256_S2_R128_B4 = 30,       // stage barrier after 4 of the last K-step's 16 MFMAs
   CFG_256_S2_R128_B12 = 31,      // ... after 12
-  CFG_COUNT = 32
+  CFG_256_S5_R64_NT = 32,        // 4 waves, 256 x 256, 5 stages of 64-byte rows (all 160 KiB), NT C
+  CFG_256_S4_R64_NT = 33,        // 4 waves, 256 x 256, 4 stages of 64-byte rows, NT C
+  CFG_COUNT = 34
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
 // kernels expand int4 to int8 on the way into LDS, 128 values per stage).
 int stage_row_bytes(KernelCfg c) {
   return (c == CFG_256_S4_R64 || c == CFG_256_S3_R64 || c == CFG_128_S4_R64 || c == CFG_PP_R64 ||
-          c == CFG_128x64_S4_R64 || c == CFG_256x128_S4_R64 || c == CFG_128x64_S8_R64)
+          c == CFG_128x64_S4_R64 || c == CFG_256x128_S4_R64 || c == CFG_128x64_S8_R64 ||
+          c == CFG_256_S5_R64_NT || c == CFG_256_S4_R64_NT)
              ? 64
              : 128;
 }
@@ -341,6 +344,12 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     case CFG_256_S2_R128_B12:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 12>, args,
                               256, stream);
+    case CFG_256_S5_R64_NT:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 5, 64, 0, false, false, 0, kNtC>, args, 256,
+                              stream);
+    case CFG_256_S4_R64_NT:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 4, 64, 0, false, false, 0, kNtC>, args, 256,
+                              stream);
     case CFG_256_S2_R128_LALL:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
     default:

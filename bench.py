@@ -38,12 +38,12 @@ if ROOT not in sys.path:
 METRIC = "INT8/INT4 TOPS and FP16 TFLOPS at N=8192 on 1 MI355X; % of MFMA peak"
 # Dense MFMA peaks of the MI355X (256 CUs, 2.4 GHz): int8 8192 ops and fp16
 # 4096 flops per CU per clock.  INT4 runs on the int8 MFMA.
-PEAK_TOPS = {"i8": 5033.2, "i4": 5033.2, "dq": 5033.2, "w8": 5033.2, "f16": 2516.6,
+PEAK_TOPS = {"i8": 5033.2, "i4": 5033.2, "dq": 5033.2, "w8": 5033.2, "w8f": 5033.2, "f16": 2516.6,
              "i4e": 5033.2, "i4g": 5033.2, "i8kn": 5033.2, "f64e": 5033.2}
 HBM_PEAK_GBS = 8000.0
-UNIT = {"i8": "TOPS", "i4": "TOPS", "dq": "TOPS", "w8": "TOPS", "f16": "TFLOPS", "i4e": "TOPS",
+UNIT = {"i8": "TOPS", "i4": "TOPS", "dq": "TOPS", "w8": "TOPS", "w8f": "TOPS", "f16": "TFLOPS", "i4e": "TOPS",
         "i4g": "TOPS", "i8kn": "TOPS", "f64e": "TFLOPS"}
-DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "w8": "i8", "f16": "f16", "i4e": "i4", "i4g": "i4",
+DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "w8": "i8", "w8f": "i8", "f16": "f16", "i4e": "i4", "i4g": "i4",
          "i8kn": "i8", "f64e": "f64"}
 KERNEL_SOURCES = ["precision_dense_gemm_02_amd/csrc/gemm_kernels.hpp",
                   "precision_dense_gemm_02_amd/csrc/lpgemm.hip"]
@@ -64,9 +64,9 @@ def parse_workload(name: str):
     if kind == "llm":
         from precision_dense_gemm_02_amd import inputs
         return "dq", size, inputs.LLM_N, inputs.LLM_K
-    if kind == "w8a8":
+    if kind in ("w8a8", "w8a8f"):
         from precision_dense_gemm_02_amd import inputs
-        return "w8", size, inputs.LLM_N, inputs.LLM_K
+        return ("w8" if kind == "w8a8" else "w8f"), size, inputs.LLM_N, inputs.LLM_K
     if kind not in ("i8", "i4", "f16", "i4e", "i4g", "i8kn", "f64e"):
         raise SystemExit(f"unknown workload {name}")
     return kind, size, size, size
@@ -170,6 +170,18 @@ class Workload:
             self.launch = lambda i: lp.gemm_f16(a, b, out=out)
             self.in_bytes = 2 * (M * K + N * K)
             self.out_bytes = 4 * M * N
+        elif kind == "w8f":
+            # the same step in one launch that quantises the rows itself
+            self.seed = inputs.seed_for("w8a8", M)
+            p = inputs.w8a8_problem(M, N, K, self.seed)
+            self.host = p
+            x, ws = to(p.x), to(p.w_scale)
+            copies = max(1, -(-336 * 2 ** 20 // (N * K)))
+            ws_list = [to(p.w) for _ in range(copies)]
+            out = torch.empty((M, N), dtype=torch.float32, device=dev)
+            self.launch = lambda i: lp.w8a8_linear_fused(x, ws_list[i % len(ws_list)], ws, out=out)
+            self.in_bytes = 2 * M * K + N * K + 4 * N
+            self.out_bytes = 4 * M * N
         elif kind == "w8":
             # fp16 activations quantised per row, then the dequantising GEMM:
             # two launches per step
@@ -226,7 +238,7 @@ class Workload:
             A, B_t = p
             ref = oracle.f64_emu(A, B_t, self.bits, rows=rows)
             ok = np.array_equal(got.view(np.uint64), ref.view(np.uint64))
-        elif self.kind == "w8":
+        elif self.kind in ("w8", "w8f"):
             q, s = oracle.quantize_rows_f16(p.x, rows=rows)
             ref = oracle.gemm_i8_dequant(q, p.w, s, p.w_scale)
             ok = np.array_equal(got.view(np.uint32), ref.view(np.uint32))
@@ -329,7 +341,7 @@ def cpu_baseline(w: Workload, seconds: float) -> dict:
             oracle.gemm_i4(p.a_packed, p.b_packed, w.K, rows=rows)
         elif w.kind == "f16":
             oracle.gemm_f16(p.a, p.b_t, rows=rows)
-        elif w.kind == "w8":
+        elif w.kind in ("w8", "w8f"):
             q, s = oracle.quantize_rows_f16(p.x, rows=rows)
             oracle.gemm_i8_dequant(q, p.w, s, p.w_scale)
         else:
@@ -400,6 +412,9 @@ def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
     if w.kind == "w8":
         rec["note"] = ("one step is two launches (per-row quantise, then the dequantising "
                        "GEMM); the kernel time and roofline cover both")
+    elif w.kind == "w8f":
+        rec["note"] = ("the W8A8 step in one launch: the GEMM quantises the rows of x itself "
+                       "(each workgroup rescans its rows for their absmax)")
     elif w.kind == "i4e":
         rec["note"] = ("int4 through the FP6 E3M2 MFMA: one step is three launches (re-encode "
                        "A, re-encode B, GEMM); the kernel time and roofline cover all three")

@@ -163,6 +163,25 @@ lpgemm_status lpgemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A
                                 const int8_t *B, const float *row_scale,
                                 const float *col_scale, float *C, hipStream_t stream);
 
+/* Largest M of lpgemm_w8a8_fused: one band of 32 rows, the decode-sized
+ * products it is meant for. */
+#define LPGEMM_W8A8_FUSED_MAX_M 32
+
+/* The W8A8 projection in one launch: C = the result of
+ * lpgemm_quantize_rows_f16(X) followed by lpgemm_i8_dequant(Q, W, row_scale,
+ * w_scale), bit for bit, without materialising Q or the row scales.  The
+ * Day-12 page weighs a quantisation prologue inside the GEMM, which repeats
+ * its work per tile, against a separate pass; this is the fused side of that
+ * comparison: every workgroup rescans its rows for their absmax and rounds
+ * each A fragment as it loads it.  X: M x K binary16 (row-major), W: N x K
+ * int8 (K-contiguous), w_scale: N floats, C: M x N fp32.  1 <= M <=
+ * LPGEMM_W8A8_FUSED_MAX_M (UNSUPPORTED_SHAPE otherwise); K as for
+ * lpgemm_i8_dequant.  X, W, C 16-byte aligned, w_scale 4-byte aligned.  M = 0
+ * or N = 0 is a no-op.  Errors as for lpgemm_i8_dequant; inf/NaN inputs are
+ * outside the contract. */
+lpgemm_status lpgemm_w8a8_fused(int64_t M, int64_t N, int64_t K, const void *X, const int8_t *W,
+                                const float *w_scale, float *C, hipStream_t stream);
+
 /* Largest K of lpgemm_quantize_rows_f16 (byte offsets within a row of X then
  * fit easily in the 32-bit offsets the kernels use). */
 #define LPGEMM_MAX_K_QUANT 1048576

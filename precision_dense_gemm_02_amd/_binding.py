@@ -61,6 +61,8 @@ def load_library():
         lib.lpgemm_i8_dequant.restype = ctypes.c_int
         lib.lpgemm_quantize_rows_f16.argtypes = [_i64, _i64, _p, _p, _p, _p]
         lib.lpgemm_quantize_rows_f16.restype = ctypes.c_int
+        lib.lpgemm_w8a8_fused.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p]
+        lib.lpgemm_w8a8_fused.restype = ctypes.c_int
         lib.lpgemm_f64_emu_moduli.argtypes = [_i64, ctypes.c_int]
         lib.lpgemm_f64_emu_moduli.restype = ctypes.c_int
         lib.lpgemm_f64_emu_workspace.argtypes = [_i64, _i64, _i64, ctypes.c_int]
@@ -271,6 +273,28 @@ def w8a8_linear(x, w, w_scale, out=None):
     function allocates) and lpgemm_i8_dequant."""
     q, s = quantize_rows_f16(x)
     return gemm_i8_dequant(q, w, s, w_scale, out=out)
+
+
+def w8a8_linear_fused(x, w, w_scale, out=None):
+    """The same result as w8a8_linear in one launch (lpgemm_w8a8_fused): the
+    kernel quantises the rows of x itself.  x fp16 M x K with M <= 32, w int8
+    N x K, w_scale fp32 N."""
+    torch = _torch()
+    _operand(x, torch.float16, "x")
+    _operand(w, torch.int8, "w")
+    if x.shape[1] != w.shape[1]:
+        raise ValueError(f"K mismatch: x {tuple(x.shape)}, w {tuple(w.shape)}")
+    M, K = x.shape
+    N = w.shape[0]
+    if not isinstance(w_scale, torch.Tensor) or w_scale.dtype != torch.float32 or w_scale.dim() != 1 \
+            or w_scale.shape[0] != N or not w_scale.is_cuda or not w_scale.is_contiguous():
+        raise ValueError(f"w_scale must be a contiguous fp32 GPU vector of length {N}")
+    dev = _same_device(x, w, w_scale)
+    out = _output(out, (M, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_w8a8_fused(M, N, K, x.data_ptr(), w.data_ptr(), w_scale.data_ptr(),
+                                                out.data_ptr(), _stream_handle(dev)), "lpgemm_w8a8_fused")
+    return out
 
 
 def i4_to_e3m2(packed, out=None):

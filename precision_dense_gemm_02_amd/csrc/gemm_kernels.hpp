@@ -1125,7 +1125,8 @@ __device__ __forceinline__ void skinny_block(typename KindTraits<KIND>::Acc (&ac
 // depend on timing) and the epilogue of the kind is applied once per element.
 template <int KIND, int MT, int NT, int WAVES, int kPitch, int kWaveWords>
 __device__ __forceinline__ void skinny_reduce_store_strided(const GemmArgs& p, const uint32_t* red,
-                                                            int m0, int n0) {
+                                                            int m0, int n0,
+                                                            const float* rs_local = nullptr) {
   for (int idx = threadIdx.x; idx < MT * NT; idx += WAVES * 64) {
     const int rr = idx / NT, cc = idx % NT;
     const int row = m0 + rr, col = n0 + cc;
@@ -1141,7 +1142,7 @@ __device__ __forceinline__ void skinny_reduce_store_strided(const GemmArgs& p, c
         ((int32_t*)p.C)[(size_t)row * p.N + col] = sum >> 8;   // undo the 16 x 16 scaling
       } else if constexpr (KIND == KIND_I8_DEQUANT) {
         float t = (float)sum;
-        t = t * p.row_scale[row];
+        t = t * (rs_local ? rs_local[rr] : p.row_scale[row]);   // the tile's scales, when local
         t = t * p.col_scale[col];
         ((float*)p.C)[(size_t)row * p.N + col] = t;
       } else {
@@ -1361,6 +1362,48 @@ __device__ __forceinline__ void load_16_async(i32x4& dst, const i32x4& rsrc, uin
 // is scheduled before the preceding wait.
 __device__ __forceinline__ void pin_after_wait(i32x4& x) { asm volatile("" : "+v"(x)); }
 
+// ---------------------------------------------------------------------------
+// Per-row int8 quantisation of fp16 activations (the step in front of a W8A8
+// projection): scale s = absmax / 127 and q = the nearest-even integer to the
+// binary32 quotient x / s, clamped to [-127, 127]; an all-zero row gets
+// s = 0 and q = 0.  The max is exact, so the order of the absmax reduction
+// does not matter.  HBM-bound: 2K bytes read and K + 4 bytes written per row.
+//
+// The quotient.  s is always RN(a / 127) for a finite fp16 a, so only about
+// 31.7 thousand scales occur.  For every one of them and every finite fp16 x
+// the sequence  r = RN(1 / s) (once per row), q0 = RN(x r),
+// e = fma(-q0, s, x), q = RN(e r + q0)  gives exactly RN(x / s) (checked
+// exhaustively on the CPU, over all 2.0e9 pairs); this is the residual
+// correction step of Markstein's division, and it costs three instructions
+// per element where a full IEEE division costs about ten.
+
+// Eight fp16 values to eight int8 codes, packed little-endian.  s must be
+// nonzero and r = RN(1 / s).
+__device__ __forceinline__ uint64_t quantize8(f16x8 h, float s, float r) {
+  uint64_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = (float)h[e];
+    const float q0 = __fmul_rn(x, r);
+    const float q = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
+    const float c = fminf(fmaxf(rintf(q), -127.f), 127.f);
+    packed |= (uint64_t)(uint8_t)(int8_t)(int)c << (8 * e);
+  }
+  return packed;
+}
+
+__device__ __forceinline__ float absmax8(f16x8 h, float amax) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)h[e]));
+  return amax;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
 // Skinny-M kernel, B through LDS as in gemm_skinny_lds, with the rounds of
 // each wave double-buffered: the copies and A loads of round i+1 are in
 // flight while round i is read back and contracted, so the weight stream
@@ -1368,16 +1411,29 @@ __device__ __forceinline__ void pin_after_wait(i32x4& x) { asm volatile("" : "+v
 // loads of the loop are inline asm (counted only by the explicit waits):
 // after issuing round i+1, vmcnt(8R) leaves exactly round i+1's 8R loads
 // outstanding, so round i has landed.
-template <int KIND, int WAVES, int R>
+//
+// QA: A holds fp16 activations (M x K binary16) that the kernel quantises
+// per row itself, the W8A8 step in one launch (KIND_I8_DEQUANT only).  Each
+// workgroup first scans the whole of its (at most 32) rows for their absmax
+// and derives the row scale s = absmax / 127 and r = 1 / s exactly as the
+// separate quantiser does; in the loop every A fragment is loaded as 16
+// halves (two 16-byte loads) and rounded to int8 with the same operations,
+// and the epilogue multiplies by the tile's scales from LDS.  The result
+// equals the separate quantiser followed by the dequantising GEMM bit for
+// bit.  The scan is repeated by every workgroup of a row band (the cost the
+// Day-12 page ascribes to a quantisation prologue inside the GEMM).
+template <int KIND, int WAVES, int R, bool QA = false>
 __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
+  static_assert(!QA || KIND == KIND_I8_DEQUANT, "on-the-fly quantisation feeds the dequantising product");
   constexpr int kBlock = 128;
   constexpr int MT = 32, NT = 32;
   constexpr int kPitch = NT + 1;
   constexpr int kBlockLds = NT * kBlock;      // 4 KiB: one K-block of the 32 B rows
   constexpr int kRoundLds = R * kBlockLds;
   constexpr int kWaveLds = 2 * kRoundLds;
-  constexpr int kLoadsPerRound = 8 * R;       // 4 copies + 4 A fragments per block
+  constexpr int kAParts = QA ? 2 : 1;         // 16-byte loads per A fragment
+  constexpr int kLoadsPerRound = (4 + 4 * kAParts) * R;   // 4 copies + the A fragments per block
   static_assert(kWaveLds >= MT * kPitch * 4, "the partial sums reuse the wave's region");
   // two rounds can be outstanding at once; the vector-memory counter holds
   // at most 63, and a wait on a counter that has overflowed passes too early
@@ -1392,13 +1448,36 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   const int m0 = tm * MT, n0 = tn * NT;
   const int rows_a = min(MT, p.M - m0);
   const int rows_b = min(NT, p.N - n0);
-  const i32x4 rsrc_a = make_rsrc(p.A + (size_t)m0 * p.row_bytes, rows_a * p.row_bytes);
+  // bytes per row of A: K (int8) or 2K (binary16)
+  const uint32_t a_stride = (uint32_t)p.row_bytes * kAParts;
+  const i32x4 rsrc_a = make_rsrc(p.A + (size_t)m0 * a_stride, rows_a * a_stride);
   const i32x4 rsrc_b = make_rsrc(p.B + (size_t)n0 * p.row_bytes, rows_b * p.row_bytes);
   uint8_t* const my_smem = smem + wave * kWaveLds;
   const uint32_t my_lds = lds_address(my_smem);
 
   const int r = lane & 31, h = lane >> 5;
   const uint32_t row_bytes = (uint32_t)p.row_bytes;
+
+  // QA: the row scale s and its reciprocal r of this lane's row r
+  __shared__ float row_amax[QA ? MT : 1];
+  __shared__ float row_s[QA ? MT : 1];
+  float qs = 0.f, qr = 0.f;
+  if constexpr (QA) {
+    for (int rr = wave; rr < MT; rr += WAVES) {
+      float amax = 0.f;
+      if (rr < rows_a) {
+        const uint8_t* xrow = p.A + (size_t)(m0 + rr) * a_stride;
+        for (uint32_t c = lane; c < row_bytes / 8; c += 64)
+          amax = absmax8(*(const f16x8*)(xrow + 16 * (size_t)c), amax);
+      }
+      amax = wave_max(amax);
+      if (lane == 0) row_amax[rr] = amax;
+    }
+    __syncthreads();
+    qs = __fdiv_rn(row_amax[r], 127.0f);
+    qr = __fdiv_rn(1.0f, qs);
+    if (wave == 0 && lane < MT) row_s[lane] = qs;   // for the epilogue, after its barrier
+  }
   const int nblk = p.k_stages;
   const int b0 = (int)(((long long)nblk * wave) / WAVES);
   const int b1 = (int)(((long long)nblk * (wave + 1)) / WAVES);
@@ -1412,7 +1491,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
     dma_off[t] = (uint32_t)row * row_bytes + c * 16;
     dma_col[t] = c * 16;
   }
-  const uint32_t a_row = (uint32_t)r * row_bytes;
+  const uint32_t a_row = (uint32_t)r * a_stride;
   int frag_off[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) frag_off[q] = r * kBlock + (swizzle_chunk(r, 4 * h + q) << 4);
@@ -1423,7 +1502,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][0][e] = 0;
 
-  i32x4 fa[2][R][1][4];
+  i32x4 fa[2][R][1][4 * kAParts];
 
   // round i: K-blocks b0 + R i .. + R - 1 into region `buf`
   auto issue = [&](int i, auto buf_c) {
@@ -1437,7 +1516,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
       for (int q = 0; q < 4; ++q) {
         const uint32_t col = kbyte + (uint32_t)h * 64 + q * 16;
         const bool ok = in_range && col < row_bytes;
-        load_16_async(fa[buf][j][0][q], rsrc_a, ok ? a_row + col : kOutOfRange);
+#pragma unroll
+        for (int part = 0; part < kAParts; ++part)
+          load_16_async(fa[buf][j][0][kAParts * q + part], rsrc_a,
+                        ok ? a_row + kAParts * col + 16 * part : kOutOfRange);
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -1463,11 +1545,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
     for (int j = 0; j < R; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        pin_after_wait(fa[buf][j][0][q]);
+#pragma unroll
+        for (int part = 0; part < kAParts; ++part) pin_after_wait(fa[buf][j][0][kAParts * q + part]);
         fb[j][q] = *(const i32x4*)(my_smem + buf * kRoundLds + j * kBlockLds + frag_off[q]);
       }
 #pragma unroll
-    for (int j = 0; j < R; ++j) skinny_block<KIND, 1>(acc[j], fa[buf][j], fb[j]);
+    for (int j = 0; j < R; ++j) {
+      if constexpr (QA) {
+        // 16 halves per fragment -> 16 int8 codes (an all-zero row: s = 0, codes 0)
+        i32x4 qa[1][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint64_t lo = qs != 0.f ? quantize8(__builtin_bit_cast(f16x8, fa[buf][j][0][2 * q]), qs, qr) : 0;
+          const uint64_t hi = qs != 0.f ? quantize8(__builtin_bit_cast(f16x8, fa[buf][j][0][2 * q + 1]), qs, qr) : 0;
+          qa[0][q] = i32x4{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
+        }
+        skinny_block<KIND, 1>(acc[j], qa, fb[j]);
+      } else {
+        skinny_block<KIND, 1>(acc[j], fa[buf][j], fb[j]);
+      }
+    }
   };
 
   if (rounds > 0) issue(0, std::integral_constant<int, 0>());
@@ -1483,7 +1580,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   wait_lgkmcnt0();
   skinny_store_partials<KIND, 1, kPitch>(acc[0], (uint32_t*)my_smem, lane);
   __syncthreads();
-  skinny_reduce_store_strided<KIND, MT, NT, WAVES, kPitch, kWaveLds / 4>(p, (const uint32_t*)smem, m0, n0);
+  skinny_reduce_store_strided<KIND, MT, NT, WAVES, kPitch, kWaveLds / 4>(p, (const uint32_t*)smem, m0, n0,
+                                                                          QA ? row_s : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1539,47 +1637,6 @@ __global__ __launch_bounds__(256) void pack_i4_e3m2(const uint8_t* __restrict__ 
   ((i32x4*)dst)[2 * g + 1] = hi;
 }
 
-// ---------------------------------------------------------------------------
-// Per-row int8 quantisation of fp16 activations (the step in front of a W8A8
-// projection): scale s = absmax / 127 and q = the nearest-even integer to the
-// binary32 quotient x / s, clamped to [-127, 127]; an all-zero row gets
-// s = 0 and q = 0.  The max is exact, so the order of the absmax reduction
-// does not matter.  HBM-bound: 2K bytes read and K + 4 bytes written per row.
-//
-// The quotient.  s is always RN(a / 127) for a finite fp16 a, so only about
-// 31.7 thousand scales occur.  For every one of them and every finite fp16 x
-// the sequence  r = RN(1 / s) (once per row), q0 = RN(x r),
-// e = fma(-q0, s, x), q = RN(e r + q0)  gives exactly RN(x / s) (checked
-// exhaustively on the CPU, over all 2.0e9 pairs); this is the residual
-// correction step of Markstein's division, and it costs three instructions
-// per element where a full IEEE division costs about ten.
-
-// Eight fp16 values to eight int8 codes, packed little-endian.  s must be
-// nonzero and r = RN(1 / s).
-__device__ __forceinline__ uint64_t quantize8(f16x8 h, float s, float r) {
-  uint64_t packed = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = (float)h[e];
-    const float q0 = __fmul_rn(x, r);
-    const float q = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
-    const float c = fminf(fmaxf(rintf(q), -127.f), 127.f);
-    packed |= (uint64_t)(uint8_t)(int8_t)(int)c << (8 * e);
-  }
-  return packed;
-}
-
-__device__ __forceinline__ float absmax8(f16x8 h, float amax) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)h[e]));
-  return amax;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
 
 // Rows of at most 512 * WPR * NC halves, held in registers: WPR wavefronts
 // share a row (a workgroup of four waves takes 4 / WPR rows) and each lane

@@ -627,6 +627,31 @@ lpgemm_status lpgemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t* A
   return run<KIND_I8_DEQUANT>(M, N, K, A, B, C, row_scale, col_scale, stream);
 }
 
+lpgemm_status lpgemm_w8a8_fused(int64_t M, int64_t N, int64_t K, const void* X, const int8_t* W,
+                                const float* w_scale, float* C, hipStream_t stream) {
+  // the dequantising product's checks, with w_scale in both scale slots (the
+  // row scales are the kernel's own)
+  bool nothing_to_do = false;
+  lpgemm_status st = validate(KIND_I8_DEQUANT, M, N, K, X, W, C, w_scale, w_scale, nothing_to_do);
+  if (st != LPGEMM_SUCCESS) return st;
+  if (M > LPGEMM_W8A8_FUSED_MAX_M) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  if (nothing_to_do) return LPGEMM_SUCCESS;
+  DeviceInfo dev;
+  st = current_device(dev);
+  if (st != LPGEMM_SUCCESS) return st;
+  GemmArgs args{};
+  args.A = static_cast<const uint8_t*>(X);
+  args.B = reinterpret_cast<const uint8_t*>(W);
+  args.C = C;
+  args.row_scale = nullptr;
+  args.col_scale = w_scale;
+  args.M = (int)M;
+  args.N = (int)N;
+  args.row_bytes = (int)K;   // of the int8 operand; the binary16 rows are twice as long
+  args.k_stages = (int)((K + 127) / 128);
+  return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND_I8_DEQUANT, 4, 1, true>, args, 256, stream);
+}
+
 lpgemm_status lpgemm_quantize_rows_f16(int64_t M, int64_t K, const void* X, int8_t* Q,
                                        float* row_scale, hipStream_t stream) {
   if (M < 0 || K < 0 || M > INT32_MAX) return LPGEMM_ERROR_INVALID_VALUE;

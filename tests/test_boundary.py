@@ -20,7 +20,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = b.declared_functions()
     assert set(names) == {"lpgemm_i8", "lpgemm_i4", "lpgemm_f16", "lpgemm_i8_dequant",
-                          "lpgemm_quantize_rows_f16", "lpgemm_i4_to_e3m2", "lpgemm_i4_e3m2",
+                          "lpgemm_quantize_rows_f16", "lpgemm_w8a8_fused", "lpgemm_i4_to_e3m2",
+                          "lpgemm_i4_e3m2",
                           "lpgemm_i8_kxn", "lpgemm_f64_emu", "lpgemm_f64_emu_moduli",
                           "lpgemm_f64_emu_workspace",
                           "lpgemm_status_string", "lpgemm_version"}
@@ -151,6 +152,25 @@ def test_quantize_validation(lib):
     assert q(4, 64, MISALIGNED, FAKE, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
     assert q(4, 64, FAKE, MISALIGNED, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
     assert q(4, 64, FAKE, FAKE, FAKE + 2, None) == b.LPGEMM_ERROR_MISALIGNED
+
+
+def test_w8a8_fused_validation(lib):
+    f = lib.lpgemm_w8a8_fused
+    assert f(-1, 64, 64, FAKE, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, -1, 64, FAKE, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 64, 24, FAKE, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE   # K % 16
+    assert f(4, 64, 131072, FAKE, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    assert f(33, 64, 64, FAKE, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE   # M > 32
+    assert f(0, 64, 64, None, None, None, None, None) == b.LPGEMM_SUCCESS       # empty: no-op
+    assert f(4, 0, 64, None, None, None, None, None) == b.LPGEMM_SUCCESS
+    assert f(4, 64, 64, None, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 64, 64, FAKE, None, FAKE, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 64, 64, FAKE, FAKE, None, FAKE, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 64, 64, FAKE, FAKE, FAKE, None, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 64, 64, MISALIGNED, FAKE, FAKE, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
+    assert f(4, 64, 64, FAKE, MISALIGNED, FAKE, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
+    assert f(4, 64, 64, FAKE, FAKE, FAKE + 2, FAKE, None) == b.LPGEMM_ERROR_MISALIGNED
+    assert f(4, 64, 64, FAKE, FAKE, FAKE, MISALIGNED, None) == b.LPGEMM_ERROR_MISALIGNED
 
 
 def test_i4_to_e3m2_validation(lib):

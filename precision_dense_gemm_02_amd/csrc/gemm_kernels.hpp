@@ -809,6 +809,17 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     uint8_t* stage_out = smem + wave * kEpiRows * kEpiPitch;
     const int row0 = m0 + wm * WTM;
     const int col0 = n0 + wn * WTN;
+    // each lane stores 16 bytes; lanes 0..WTN/4-1 cover one row
+    constexpr int kLanesPerRow = WTN / 4;
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    // dequant: the column scales of this lane's four output columns (the
+    // same in every row it stores)
+    float cs4[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KIND == KIND_I8_DEQUANT) {
+      const int cl = col0 + (lane % kLanesPerRow) * 4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) cs4[x] = p.col_scale[cl + x];
+    }
 #pragma unroll
     for (int half = 0; half < TM / 2; ++half) {
       // accumulator blocks i = 2*half, 2*half+1 cover 64 rows of the quadrant
@@ -821,19 +832,39 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
           for (int e = 0; e < 16; ++e) {
             const int r = ii * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
             const int c = j * 32 + fr;
+            // dequant: the raw sums go through LDS; the scales are applied
+            // as the rows are stored
             *(uint32_t*)(stage_out + r * kEpiPitch + c * 4) =
-                value(i, j, e, row0 + half * 64 + r, col0 + c);
+                KIND == KIND_I8_DEQUANT ? (uint32_t)acc[i][j][e] : value(i, j, e, row0 + half * 64 + r, col0 + c);
           }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes done
-      // each lane stores 16 bytes; lanes 0..WTN/4-1 cover one row
-      constexpr int kLanesPerRow = WTN / 4;
-      constexpr int kRowsPerStore = 64 / kLanesPerRow;
+      // dequant: lane l holds the scale of row l of these 64 (inside M: the
+      // tile is interior); each store's rows take theirs by lane index
+      float rs_half = 0.f;
+      if constexpr (KIND == KIND_I8_DEQUANT) rs_half = p.row_scale[row0 + half * 64 + lane];
 #pragma unroll
       for (int r0 = 0; r0 < kEpiRows; r0 += kRowsPerStore) {
         const int r = r0 + lane / kLanesPerRow;
         const int c = (lane % kLanesPerRow) * 4;
-        const i32x4 v = *(const i32x4*)(stage_out + r * kEpiPitch + c * 4);
+        i32x4 v = *(const i32x4*)(stage_out + r * kEpiPitch + c * 4);
+        if constexpr (KIND == KIND_I8_DEQUANT) {
+          // ((float)acc * row_scale) * col_scale, each product rounded once
+          float rs = 0.f;
+#pragma unroll
+          for (int q = 0; q < kRowsPerStore; ++q) {
+            const float sq = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rs_half), r0 + q));
+            if (lane / kLanesPerRow == q) rs = sq;
+          }
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            float t = (float)v[x];
+            t = t * rs;
+            t = t * cs4[x];
+            v[x] = __builtin_bit_cast(int, t);
+          }
+        }
         const size_t idx = (size_t)(row0 + half * 64 + r) * p.N + col0 + c;
         if constexpr (NTC) __builtin_nontemporal_store(v, (i32x4*)((uint32_t*)p.C + idx));
         else *(i32x4*)((uint32_t*)p.C + idx) = v;

@@ -426,6 +426,49 @@ def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
     return w, rec
 
 
+def platform_library(steps: int, warmup: int, n: int = 8192) -> list:
+    """torch's own GEMMs on this GPU (hipBLASLt under ROCm) at n^3, timed with
+    the same steady-state protocol as the headline: context for the measured
+    fraction of peak, not the target.  Operand layouts are the library's:
+    torch._int_mm takes B as K x N; torch.matmul on fp16 returns fp16 (half
+    the output bytes of the fp32-output kernel here)."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    out = []
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ops = 2 * n ** 3
+    a = torch.randint(-128, 128, (n, n), dtype=torch.int8, device=dev, generator=g)
+    b = torch.randint(-128, 128, (n, n), dtype=torch.int8, device=dev, generator=g)
+    try:
+        ms = timed(lambda: torch._int_mm(a, b))
+        out.append({"op": f"torch._int_mm int8 {n}^3, int32 out", "ms": round(ms, 5),
+                    "value": round(ops / ms / 1e9, 1), "unit": "TOPS"})
+    except RuntimeError as e:
+        out.append({"op": f"torch._int_mm int8 {n}^3", "error": str(e)[:200]})
+    del a, b
+    a = torch.randn((n, n), device=dev, generator=g).half()
+    b = torch.randn((n, n), device=dev, generator=g).half()
+    ms = timed(lambda: torch.matmul(a, b))
+    out.append({"op": f"torch.matmul fp16 {n}^3, fp32 accumulation, fp16 out", "ms": round(ms, 5),
+                "value": round(ops / ms / 1e9, 1), "unit": "TFLOPS"})
+    return out
+
+
 # the kernel each square workload runs at 8192 (configuration 0)
 TRAFFIC_KERNELS = {
     "i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0>(lpgemm::GemmArgs)",
@@ -481,6 +524,8 @@ def main():
                     help="time the steps as one captured HIP graph (GPU time without host "
                          "launch overhead; for the small shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-platform", action="store_true",
+                    help="skip timing torch's own int8 / fp16 GEMMs at 8192 (context)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (--steps times); its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the traffic figures")
@@ -533,6 +578,12 @@ def main():
         print(f"# cpu oracle: {cpu['value']} {cpu['unit']} on {cpu['cores']} threads",
               file=sys.stderr, flush=True)
 
+    platform = None
+    if not args.no_platform and not args.graph and args.workload == "i8-8192":
+        platform = platform_library(args.steps, args.warmup)
+        for r in platform:
+            print(f"# platform library: {r}", file=sys.stderr, flush=True)
+
     line = {
         "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
@@ -547,6 +598,7 @@ def main():
         "cpu_baseline": cpu,
         **{k: head[k] for k in ("note", "precision_contract", "native_f64_matmul") if k in head},
         "also": also,
+        "platform_library": platform,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -469,6 +469,18 @@ struct RowLayout<128> {
   __device__ static int pos(int r, int c) { return swizzle_chunk(r, c); }
 };
 
+// 256-byte rows: 16 chunks; the chunk position XORs the row's low 4 bits,
+// so the 16 consecutive rows one 16-lane group of a fragment read touches
+// (one chunk each) sit on distinct chunk positions: conflict-free at 64
+// banks, and at 32 banks for every 8 consecutive rows.  Longer rows let one
+// stage take 256 contiguous bytes of each operand row from HBM.
+template <>
+struct RowLayout<256> {
+  static constexpr int kChunks = 16;
+  __device__ static int off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+  __device__ static int pos(int r, int c) { return c ^ (r & 15); }
+};
+
 // 64-byte rows: 4 chunks; pairs of rows share a 128-byte line.  The chunk
 // position XORs a 2-bit function of the line chosen so that rows m, m+4,
 // m+8, m+12 (which share banks at 64 banks) and rows of one parity among 8

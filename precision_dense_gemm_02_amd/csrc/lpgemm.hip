@@ -123,7 +123,10 @@ enum KernelCfg {
   CFG_256_S2_R128_B12 = 31,      // ... after 12
   CFG_256_S5_R64_NT = 32,        // 4 waves, 256 x 256, 5 stages of 64-byte rows (all 160 KiB), NT C
   CFG_256_S4_R64_NT = 33,        // 4 waves, 256 x 256, 4 stages of 64-byte rows, NT C
-  CFG_COUNT = 34
+  CFG_128x64_S3_R256 = 34,       // 4 waves, 128 x 64, 3 stages of 256-byte rows
+  CFG_128_S5_R128 = 35,          // 4 waves, 128 x 128, 5 stages of 128-byte rows (all 160 KiB)
+  CFG_128_S2_R256 = 36,          // 4 waves, 128 x 128, 2 stages of 256-byte rows
+  CFG_COUNT = 37
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -133,7 +136,7 @@ int stage_row_bytes(KernelCfg c) {
           c == CFG_128x64_S4_R64 || c == CFG_256x128_S4_R64 || c == CFG_128x64_S8_R64 ||
           c == CFG_256_S5_R64_NT || c == CFG_256_S4_R64_NT)
              ? 64
-             : 128;
+             : ((c == CFG_128x64_S3_R256 || c == CFG_128_S2_R256) ? 256 : 128);
 }
 bool expands_int4_in_lds(KernelCfg c) { return c >= CFG_V1_256x256 && c <= CFG_V1_64x64; }
 bool is_skinny(KernelCfg c) { return c >= CFG_SKINNY_32 && c <= CFG_SKINNY_PIPE_W8R2; }
@@ -167,19 +170,24 @@ KernelCfg choose_config_e3m2(int64_t M, int64_t N, int cu_count) {
   return CFG_128x64_S6_R128;
 }
 
-KernelCfg choose_config(int64_t M, int64_t N, int cu_count) {
+KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   const int f = forced_config();
   if (f >= 0) return (KernelCfg)f;
+  const bool int8_rows = kind == KIND_I8 || kind == KIND_I8_DEQUANT;
   // few rows against many columns: stream B with split-K workgroups
   if (M <= 32) return CFG_SKINNY_PIPE_W4R2;
   if (M <= 64) return CFG_SKINNY_64;
-  // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128, and
-  // six 128-byte stages keep more of the streamed B operand in flight
-  if (M <= 128) return CFG_128x64_S6_R128;
+  // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128.
+  // int8 rows stream B in 256-byte pieces per stage (M = 128, K = 4096,
+  // N = 14336: 19.2 us against 20.4 us with six 128-byte stages)
+  if (M <= 128) return int8_rows ? CFG_128x64_S3_R256 : CFG_128x64_S6_R128;
   const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
   if (big >= cu_count) return CFG_256_S2_R128;
+  // 128 x 128 tiles: at 2048^3, two 256-byte stages for int8 and int4
+  // (14.5 / 15.0 us against 15.4 / 15.7 us with four 64-byte stages), four
+  // 128-byte stages for fp16 (23.1 against 25.4 us)
   const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
-  if (mid >= cu_count / 2) return CFG_128_S4_R64;
+  if (mid >= cu_count / 2) return kind == KIND_F16 ? CFG_128_S4_R128 : CFG_128_S2_R256;
   return CFG_V1_64x64;
 }
 
@@ -242,7 +250,7 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
 
   const KernelCfg cfg = BKN ? choose_config_kxn(M, N, dev.cu_count)
                       : (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) ? choose_config_e3m2(M, N, dev.cu_count)
-                                             : choose_config(M, N, dev.cu_count);
+                                             : choose_config(M, N, dev.cu_count, KIND);
   const int64_t stage_bytes = (KIND == KIND_I4 && expands_int4_in_lds(cfg)) ? K : row_bytes;
   (void)is_skinny;
   const int rowb = stage_row_bytes(cfg);
@@ -324,6 +332,12 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128>, args, 256, stream);
     case CFG_128x64_S8_R64:
       return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 8, 64>, args, 256, stream);
+    case CFG_128x64_S3_R256:
+      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 3, 256>, args, 256, stream);
+    case CFG_128_S5_R128:
+      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 5, 128>, args, 256, stream);
+    case CFG_128_S2_R256:
+      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 2, 256>, args, 256, stream);
     case CFG_256_S2_R128_NT:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 1>, args, 256, stream);
     case CFG_256_S2_R128_SC0:

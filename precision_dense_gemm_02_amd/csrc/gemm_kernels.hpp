@@ -415,6 +415,23 @@ __device__ __forceinline__ void lds_dma_16(const i32x4& rsrc, uint32_t lds_addr,
 #undef LPGEMM_LDS_DMA
 }
 
+// The same transfer at 4 bytes per lane (lane l's word lands at lds_addr +
+// 4 l).  Used to pull operand lines into the L2 ahead of their real loads:
+// the words land in an LDS area nobody reads, so there is no register result
+// to track and nothing for the compiler to drop.
+__device__ __forceinline__ void lds_dma_4(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
@@ -516,8 +533,13 @@ struct RowLayout<64> {
 // stage's loads are issued (0: all but the last K-step).  NTC: C is written
 // with non-temporal stores.  BSPLIT: MFMAs of the last K-step issued before
 // the stage barrier (0: half).
+//
+// PF: during stage s, after the loads of stage s + STAGES - 1, touch one word
+// of every operand row's stage s + STAGES chunk (one 64-row load per 64 rows,
+// into a 256-byte LDS sink), so that the chunk's lines are on their way to
+// the L2 one stage before the real loads ask for them.
 template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false,
-          bool BKN = false, int LSTEPS = 0, bool NTC = false, int BSPLIT = 0>
+          bool BKN = false, int LSTEPS = 0, bool NTC = false, int BSPLIT = 0, bool PF = false>
 __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
@@ -548,8 +570,13 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   constexpr int kEpiPitch = WTN * 4 + 32;
   constexpr int kEpiRows = 64;
   constexpr int kEpiLds = 4 * kEpiRows * kEpiPitch;
-  constexpr int kLds = kMainLds > kEpiLds ? kMainLds : kEpiLds;
+  constexpr int kLds0 = kMainLds > kEpiLds ? kMainLds : kEpiLds;
+  // prefetch: 64-row touches per wave per stage, and their LDS sink
+  static_assert(!PF || (!BKN && BM % 64 == 0 && (BM + BN) % 256 == 0), "prefetch rows");
+  constexpr int kPf = PF ? (BM + BN) / 256 : 0;
+  constexpr int kLds = kLds0 + (PF ? 256 : 0);
   static_assert(kLds <= 160 * 1024, "LDS");
+  static_assert((STAGES - 2) * kSlots + kPf <= 63, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
 
@@ -624,6 +651,22 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       off = in_row ? slot_off[t] + kbyte : kOutOfRange;
     }
     lds_dma_16<CPOL>(is_a(t) ? rsrc_a : rsrc_b, smem_lds + (s % STAGES) * kStage + g * 1024, off);
+  };
+
+  // prefetch touch t of this wave covers operand rows 64 (kPf wave + t) ..
+  // + 63 (A's rows first), one row per lane, at the row's first word of the
+  // stage's chunk
+  auto issue_prefetch = [&](int s) {
+    const uint32_t kbyte = (uint32_t)s * ROWB;
+#pragma unroll
+    for (int t = 0; t < kPf; ++t) {
+      const int r = 64 * (kPf * wave + t) + lane;
+      const bool a_rows = 64 * (kPf * wave + t) < BM;
+      const uint32_t off = kbyte < (uint32_t)p.row_bytes
+                               ? (uint32_t)(a_rows ? r : r - BM) * (uint32_t)p.row_bytes + kbyte
+                               : kOutOfRange;
+      lds_dma_4(a_rows ? rsrc_a : rsrc_b, smem_lds + kLds0, off);
+    }
   };
 
   // Fragment addressing: lane l reads row (l & 31) of a 32-row block; blocks
@@ -747,13 +790,17 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   };
 
   const int nks = p.k_stages;   // 0 when K = 0: C is written as zeros
+  // the prefetch of stage s + STAGES is issued in this K-step of stage s,
+  // after the stage's own loads
+  constexpr int kPfStep = kLoadSteps < KSTEPS - 1 ? kLoadSteps : KSTEPS - 1;
   if (nks > 0) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
 #pragma unroll
       for (int t = 0; t < kSlots; ++t) issue_load(t, s);
-    wait_vmcnt<(STAGES - 2) * kSlots>();   // own loads of stage 0
-    block_barrier();                       // everyone's
+    if constexpr (PF) issue_prefetch(STAGES - 1);
+    wait_vmcnt<(STAGES - 2) * kSlots + kPf>();   // own loads of stage 0
+    block_barrier();                             // everyone's
     read_frags(0, 0, 0);
   }
   for (int s = 0; s < nks; ++s) {
@@ -772,6 +819,12 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
           ++nl;
         }
       }
+      if constexpr (PF) {
+        if (kk == kPfStep) {
+          issue_prefetch(s + STAGES);
+          nl += kPf;
+        }
+      }
       if (kk + 1 < KSTEPS) {
         read_frags(s, kk + 1, dst);
         compute(src, 0, kMfma);
@@ -780,7 +833,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
         compute(src, 0, kSplit);
         interleave(kSplit, 0, nl);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<(STAGES - 2) * kSlots>();   // own loads of stage s+1 landed
+        wait_vmcnt<(STAGES - 2) * kSlots + kPf>();   // own loads of stage s+1 landed
         wait_lgkmcnt0();                       // own reads of stage s done
         block_barrier();                       // ... everyone's
         read_frags(s + 1, 0, dst);
@@ -793,18 +846,15 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   // ------------------------------------------------------------------ epilogue
   // Element e of lane l in a 32x32 block is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32 of the block.
-  auto value = [&](int i, int j, int e, int row, int col) -> uint32_t {
+  // The value a lane stages for accumulator element e of block (i, j); the
+  // dequant kind stages the raw sum and scales it when storing
+  auto value = [&](int i, int j, int e) -> uint32_t {
     if constexpr (KIND == KIND_F16) {
       return __builtin_bit_cast(uint32_t, (float)acc[i][j][e]);
     } else if constexpr (E3M2) {
       return (uint32_t)(int32_t)acc[i][j][e];   // an integer below 2^24: exact
     } else if constexpr (KIND == KIND_I4) {
       return (uint32_t)(acc[i][j][e] >> 8);   // undo the 16 x 16 scaling
-    } else if constexpr (KIND == KIND_I8_DEQUANT) {
-      float t = (float)acc[i][j][e];
-      t = t * p.row_scale[row];
-      t = t * p.col_scale[col];
-      return __builtin_bit_cast(uint32_t, t);
     } else {
       return (uint32_t)acc[i][j][e];
     }
@@ -814,9 +864,13 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   // reused; the barrier then also covers every wave's fragment reads.
   wait_vmcnt<0>();
   wait_lgkmcnt0();
-  // the reduced kind stores bytes through the direct path below
-  const bool interior = KIND != KIND_I8_MOD && m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 3) == 0;
-  if (interior) {
+  if constexpr (KIND != KIND_I8_MOD) {
+    // Every kind but the reduced one goes through LDS: each wave transposes
+    // 64 rows of its quadrant at a time so that a lane holds 4 consecutive
+    // columns of one row.  A tile inside C whose rows start 16-byte aligned
+    // (N % 4 == 0) writes them with 16-byte stores; an edge tile writes each
+    // value inside C with its own 4-byte store.
+    const bool full = m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 3) == 0;
     block_barrier();   // every wave is done with the operand stages
     uint8_t* stage_out = smem + wave * kEpiRows * kEpiPitch;
     const int row0 = m0 + wm * WTM;
@@ -824,13 +878,14 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     // each lane stores 16 bytes; lanes 0..WTN/4-1 cover one row
     constexpr int kLanesPerRow = WTN / 4;
     constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    const int c_lane = (lane % kLanesPerRow) * 4;
     // dequant: the column scales of this lane's four output columns (the
-    // same in every row it stores)
+    // same in every row it stores; zero outside C)
     float cs4[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (KIND == KIND_I8_DEQUANT) {
-      const int cl = col0 + (lane % kLanesPerRow) * 4;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) cs4[x] = p.col_scale[cl + x];
+      for (int x = 0; x < 4; ++x)
+        if (col0 + c_lane + x < p.N) cs4[x] = p.col_scale[col0 + c_lane + x];
     }
 #pragma unroll
     for (int half = 0; half < TM / 2; ++half) {
@@ -847,19 +902,21 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
             // dequant: the raw sums go through LDS; the scales are applied
             // as the rows are stored
             *(uint32_t*)(stage_out + r * kEpiPitch + c * 4) =
-                KIND == KIND_I8_DEQUANT ? (uint32_t)acc[i][j][e] : value(i, j, e, row0 + half * 64 + r, col0 + c);
+                KIND == KIND_I8_DEQUANT ? (uint32_t)acc[i][j][e] : value(i, j, e);
           }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes done
-      // dequant: lane l holds the scale of row l of these 64 (inside M: the
-      // tile is interior); each store's rows take theirs by lane index
+      // dequant: lane l holds the scale of row l of these 64 (zero outside
+      // C); each store's rows take theirs by lane index
       float rs_half = 0.f;
-      if constexpr (KIND == KIND_I8_DEQUANT) rs_half = p.row_scale[row0 + half * 64 + lane];
+      if constexpr (KIND == KIND_I8_DEQUANT) {
+        const int rl = row0 + half * 64 + lane;
+        if (rl < p.M) rs_half = p.row_scale[rl];
+      }
 #pragma unroll
       for (int r0 = 0; r0 < kEpiRows; r0 += kRowsPerStore) {
         const int r = r0 + lane / kLanesPerRow;
-        const int c = (lane % kLanesPerRow) * 4;
-        i32x4 v = *(const i32x4*)(stage_out + r * kEpiPitch + c * 4);
+        i32x4 v = *(const i32x4*)(stage_out + r * kEpiPitch + c_lane * 4);
         if constexpr (KIND == KIND_I8_DEQUANT) {
           // ((float)acc * row_scale) * col_scale, each product rounded once
           float rs = 0.f;
@@ -877,13 +934,22 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
             v[x] = __builtin_bit_cast(int, t);
           }
         }
-        const size_t idx = (size_t)(row0 + half * 64 + r) * p.N + col0 + c;
-        if constexpr (NTC) __builtin_nontemporal_store(v, (i32x4*)((uint32_t*)p.C + idx));
-        else *(i32x4*)((uint32_t*)p.C + idx) = v;
+        const int grow = row0 + half * 64 + r;
+        const int gcol = col0 + c_lane;
+        uint32_t* dst = (uint32_t*)p.C + (size_t)grow * p.N + gcol;
+        if (full) {
+          if constexpr (NTC) __builtin_nontemporal_store(v, (i32x4*)dst);
+          else *(i32x4*)dst = v;
+        } else if (grow < p.M) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if (gcol + x < p.N) dst[x] = (uint32_t)v[x];
+        }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next half overwrites
     }
   } else {
+    // the reduced kind: one byte per value, straight from the accumulators
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -893,7 +959,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
         for (int e = 0; e < 16; ++e) {
           const int row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
           if (col < p.N && row < p.M) {
-            if constexpr (KIND == KIND_I8_MOD) {
+            {
               // the non-negative residue: |acc| < 2^31 is exact in double, q
               // from the rounded reciprocal is within one of floor(acc / m),
               // fma(-q, m, acc) is exact, and one correction each way ends it
@@ -902,8 +968,6 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
               if (r < 0.0) r += m;
               if (r >= m) r -= m;
               ((uint8_t*)p.C)[(size_t)row * p.N + col] = (uint8_t)(int)r;
-            } else {
-              ((uint32_t*)p.C)[(size_t)row * p.N + col] = value(i, j, e, row, col);
             }
           }
         }

@@ -126,7 +126,8 @@ enum KernelCfg {
   CFG_128x64_S3_R256 = 34,       // 4 waves, 128 x 64, 3 stages of 256-byte rows
   CFG_128_S5_R128 = 35,          // 4 waves, 128 x 128, 5 stages of 128-byte rows (all 160 KiB)
   CFG_128_S2_R256 = 36,          // 4 waves, 128 x 128, 2 stages of 256-byte rows
-  CFG_COUNT = 37
+  CFG_256_S2_R128_PF = 37,       // configuration 0 plus an L2 prefetch of the stage after next
+  CFG_COUNT = 38
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -338,6 +339,9 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 5, 128>, args, 256, stream);
     case CFG_128_S2_R256:
       return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 2, 256>, args, 256, stream);
+    case CFG_256_S2_R128_PF:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, true>, args, 256, stream);
     case CFG_256_S2_R128_NT:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 1>, args, 256, stream);
     case CFG_256_S2_R128_SC0:

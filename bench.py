@@ -471,9 +471,9 @@ def platform_library(steps: int, warmup: int, n: int = 8192) -> list:
 
 # the kernel each square workload runs at 8192 (configuration 0)
 TRAFFIC_KERNELS = {
-    "i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false>(lpgemm::GemmArgs)",
-    "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false>(lpgemm::GemmArgs)",
-    "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false>(lpgemm::GemmArgs)"}
+    "i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true>(lpgemm::GemmArgs)",
+    "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false>(lpgemm::GemmArgs)",
+    "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true>(lpgemm::GemmArgs)"}
 
 
 def _median_counter(path: str, kernel: str, counter: str) -> float:

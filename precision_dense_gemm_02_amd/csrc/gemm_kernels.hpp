@@ -534,12 +534,18 @@ struct RowLayout<64> {
 // with non-temporal stores.  BSPLIT: MFMAs of the last K-step issued before
 // the stage barrier (0: half).
 //
+// HIL: in a K-step that issues loads, pin one MFMA in front of each load
+// (the scheduler does not see the inline-asm loads as memory reads, so left
+// alone it issues a K-step's loads back to back ahead of its MFMAs).  Not
+// for int4: the pinned order keeps every expanded operand live and spills.
+//
 // PF: during stage s, after the loads of stage s + STAGES - 1, touch one word
 // of every operand row's stage s + STAGES chunk (one 64-row load per 64 rows,
 // into a 256-byte LDS sink), so that the chunk's lines are on their way to
 // the L2 one stage before the real loads ask for them.
 template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false,
-          bool BKN = false, int LSTEPS = 0, bool NTC = false, int BSPLIT = 0, bool PF = false>
+          bool BKN = false, int LSTEPS = 0, bool NTC = false, int BSPLIT = 0, bool PF = false,
+          bool HIL = false>
 __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
@@ -554,6 +560,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   static_assert(KSTEPS % 2 == 0, "K-steps per stage must be even");
   static_assert(!BKN || KIND == KIND_I8 || KIND == KIND_I8_DEQUANT, "K x N storage of B is int8 only");
   static_assert(!BKN || !SPLIT, "one ablation at a time");
+  static_assert(!HIL || !I4, "the pinned interleave spills int4's expanded operands");
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM % 2 == 0 && TN >= 1 && BM % 128 == 0 && BN % 64 == 0, "tile");
@@ -811,12 +818,23 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     for (int kk = 0; kk < KSTEPS; ++kk) {
       const int src = kk & 1, dst = src ^ 1;
       int nl = 0;
+      int pre = 0;   // MFMAs already issued in front of this K-step's loads
       if (kk < kLoadSteps) {
 #pragma unroll
         for (int t = 0; t < kSlots; ++t) {
           if (t / kLoadsPerStep != kk) continue;
-          issue_load(t, sl);
-          ++nl;
+          if constexpr (HIL) {
+            if (pre < (kk + 1 < KSTEPS ? kMfma : kSplit)) {
+              compute(src, pre, pre + 1);
+              ++pre;
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            issue_load(t, sl);
+            __builtin_amdgcn_sched_barrier(0);
+          } else {
+            issue_load(t, sl);
+            ++nl;
+          }
         }
       }
       if constexpr (PF) {
@@ -827,11 +845,11 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       }
       if (kk + 1 < KSTEPS) {
         read_frags(s, kk + 1, dst);
-        compute(src, 0, kMfma);
-        interleave(kMfma, kReads, nl);
+        compute(src, pre, kMfma);
+        interleave(kMfma - pre, kReads, nl);
       } else {
-        compute(src, 0, kSplit);
-        interleave(kSplit, 0, nl);
+        compute(src, pre, kSplit);
+        interleave(kSplit - pre, 0, nl);
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<(STAGES - 2) * kSlots + kPf>();   // own loads of stage s+1 landed
         wait_lgkmcnt0();                       // own reads of stage s done

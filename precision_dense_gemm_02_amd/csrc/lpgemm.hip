@@ -127,7 +127,11 @@ enum KernelCfg {
   CFG_128_S5_R128 = 35,          // 4 waves, 128 x 128, 5 stages of 128-byte rows (all 160 KiB)
   CFG_128_S2_R256 = 36,          // 4 waves, 128 x 128, 2 stages of 256-byte rows
   CFG_256_S2_R128_PF = 37,       // configuration 0 plus an L2 prefetch of the stage after next
-  CFG_COUNT = 38
+  CFG_256_S2_R128_SCHED = 38,    // configuration 0 with the loads placed by the compiler's schedule
+  CFG_128_S2_R256_PIN = 39,      // configuration 36 with one MFMA pinned in front of each load
+  CFG_128_S4_R128_PIN = 40,      // configuration 22 with one MFMA pinned in front of each load
+  CFG_128x64_S3_R256_PIN = 41,   // configuration 34 with one MFMA pinned in front of each load
+  CFG_COUNT = 42
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -263,6 +267,10 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   // apply.  On the general and K x N paths it also issues the next stage's
   // loads in its first two K-steps (int8 +1.5%, fp16 +2%).
   constexpr bool kNtC = KIND != KIND_I4 && KIND != KIND_I8_MOD;
+  // ... and pins one MFMA in front of each of a K-step's loads (8192^3 on one
+  // box: int8 2306 against 2271 TOP/s, fp16 1221 against 1182 TFLOP/s),
+  // except for int4, whose expanded operands would then spill
+  constexpr bool kPinLoads = KIND != KIND_I4;
 
   if constexpr (BKN) {
     switch (cfg) {
@@ -289,8 +297,9 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   } else {
   switch (cfg) {
     case CFG_256_S2_R128:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC>, args,
-                              256, stream);
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads>, args, 256,
+          stream);
     case CFG_128_S4_R128:
       return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
     case CFG_256_S4_R64:
@@ -339,6 +348,22 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 5, 128>, args, 256, stream);
     case CFG_128_S2_R256:
       return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 2, 256>, args, 256, stream);
+    case CFG_128_S2_R256_PIN:
+      return launch<128, 128>(
+          (const void*)&gemm_v3<KIND, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_128_S4_R128_PIN:
+      return launch<128, 128>(
+          (const void*)&gemm_v3<KIND, 128, 128, 4, 128, 0, false, false, 0, false, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_128x64_S3_R256_PIN:
+      return launch<128, 64>(
+          (const void*)&gemm_v3<KIND, 128, 64, 3, 256, 0, false, false, 0, false, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_256_S2_R128_SCHED:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, false>, args, 256,
+          stream);
     case CFG_256_S2_R128_PF:
       return launch<256, 256>(
           (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, true>, args, 256, stream);

@@ -131,7 +131,9 @@ enum KernelCfg {
   CFG_128_S2_R256_PIN = 39,      // configuration 36 with one MFMA pinned in front of each load
   CFG_128_S4_R128_PIN = 40,      // configuration 22 with one MFMA pinned in front of each load
   CFG_128x64_S3_R256_PIN = 41,   // configuration 34 with one MFMA pinned in front of each load
-  CFG_COUNT = 42
+  CFG_256_S2_R128_PIN_L1 = 42,   // configuration 0 with all of a stage's loads pinned in K-step 0
+  CFG_256_S2_R128_PIN_L3 = 43,   // configuration 0 with the loads pinned over K-steps 0-2
+  CFG_COUNT = 44
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -359,6 +361,14 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     case CFG_128x64_S3_R256_PIN:
       return launch<128, 64>(
           (const void*)&gemm_v3<KIND, 128, 64, 3, 256, 0, false, false, 0, false, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_256_S2_R128_PIN_L1:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 1, kNtC, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_256_S2_R128_PIN_L3:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 3, kNtC, 0, false, kPinLoads>, args, 256,
           stream);
     case CFG_256_S2_R128_SCHED:
       return launch<256, 256>(

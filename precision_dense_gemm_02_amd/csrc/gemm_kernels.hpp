@@ -536,8 +536,8 @@ struct RowLayout<64> {
 //
 // HIL: in a K-step that issues loads, pin one MFMA in front of each load
 // (the scheduler does not see the inline-asm loads as memory reads, so left
-// alone it issues a K-step's loads back to back ahead of its MFMAs).  Not
-// for int4: the pinned order keeps every expanded operand live and spills.
+// alone it issues a K-step's loads back to back ahead of its MFMAs).  int4
+// then expands a K-step's operands once, before the pinned MFMAs.
 //
 // PF: during stage s, after the loads of stage s + STAGES - 1, touch one word
 // of every operand row's stage s + STAGES chunk (one 64-row load per 64 rows,
@@ -560,7 +560,9 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   static_assert(KSTEPS % 2 == 0, "K-steps per stage must be even");
   static_assert(!BKN || KIND == KIND_I8 || KIND == KIND_I8_DEQUANT, "K x N storage of B is int8 only");
   static_assert(!BKN || !SPLIT, "one ablation at a time");
-  static_assert(!HIL || !I4, "the pinned interleave spills int4's expanded operands");
+  // int4 with pinned loads expands a K-step's operands once, ahead of the
+  // pinned MFMAs, so that they are not rebuilt between scheduling barriers
+  constexpr bool kOnce = HIL && I4;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM % 2 == 0 && TN >= 1 && BM % 128 == 0 && BN % 64 == 0, "tile");
@@ -763,12 +765,8 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-  auto compute = [&](int src, int first, int last) {
-    Op a[TM], b[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = operand(fa[src][i]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = operand(fb[src][j]);
+  // MFMAs first .. last-1 of a K-step on operands already in MFMA form
+  auto compute_ops = [&](const Op (&a)[TM], const Op (&b)[TN], int first, int last) {
 #pragma unroll
     for (int x = 0; x < TM * TN; ++x) {
       if (x < first || x >= last) continue;
@@ -776,6 +774,15 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       if constexpr (E3M2) acc[i][j] = mfma_e3m2(a[i], b[j], acc[i][j]);
       else acc[i][j] = mfma<KIND>(a[i], b[j], acc[i][j]);
     }
+  };
+  // ... on fragment buffer src, converted here (int4: expanded to int8)
+  auto compute = [&](int src, int first, int last) {
+    Op a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = operand(fa[src][i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = operand(fb[src][j]);
+    compute_ops(a, b, first, last);
   };
 
   constexpr int kMfma = TM * TN;
@@ -817,6 +824,17 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       const int src = kk & 1, dst = src ^ 1;
+      Op ea[TM], eb[TN];
+      if constexpr (kOnce) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) ea[i] = operand(fa[src][i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) eb[j] = operand(fb[src][j]);
+      }
+      auto mm = [&](int first, int last) {
+        if constexpr (kOnce) compute_ops(ea, eb, first, last);
+        else compute(src, first, last);
+      };
       int nl = 0;
       int pre = 0;   // MFMAs already issued in front of this K-step's loads
       if (kk < kLoadSteps) {
@@ -825,7 +843,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
           if (t / kLoadsPerStep != kk) continue;
           if constexpr (HIL) {
             if (pre < (kk + 1 < KSTEPS ? kMfma : kSplit)) {
-              compute(src, pre, pre + 1);
+              mm(pre, pre + 1);
               ++pre;
               __builtin_amdgcn_sched_barrier(0);
             }
@@ -845,17 +863,17 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       }
       if (kk + 1 < KSTEPS) {
         read_frags(s, kk + 1, dst);
-        compute(src, pre, kMfma);
+        mm(pre, kMfma);
         interleave(kMfma - pre, kReads, nl);
       } else {
-        compute(src, pre, kSplit);
+        mm(pre, kSplit);
         interleave(kSplit - pre, 0, nl);
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<(STAGES - 2) * kSlots + kPf>();   // own loads of stage s+1 landed
         wait_lgkmcnt0();                       // own reads of stage s done
         block_barrier();                       // ... everyone's
         read_frags(s + 1, 0, dst);
-        compute(src, kSplit, kMfma);
+        mm(kSplit, kMfma);
         interleave(kMfma - kSplit, kReads, 0);
       }
     }

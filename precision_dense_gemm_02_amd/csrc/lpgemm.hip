@@ -133,7 +133,8 @@ enum KernelCfg {
   CFG_128x64_S3_R256_PIN = 41,   // configuration 34 with one MFMA pinned in front of each load
   CFG_256_S2_R128_PIN_L1 = 42,   // configuration 0 with all of a stage's loads pinned in K-step 0
   CFG_256_S2_R128_PIN_L3 = 43,   // configuration 0 with the loads pinned over K-steps 0-2
-  CFG_COUNT = 44
+  CFG_256_S2_R128_PIN_I4 = 44,   // configuration 0 with pinned loads also for int4
+  CFG_COUNT = 45
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -369,6 +370,10 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     case CFG_256_S2_R128_PIN_L3:
       return launch<256, 256>(
           (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 3, kNtC, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_256_S2_R128_PIN_I4:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, true>, args, 256,
           stream);
     case CFG_256_S2_R128_SCHED:
       return launch<256, 256>(

@@ -270,8 +270,8 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   // apply.  On the general and K x N paths it also issues the next stage's
   // loads in its first two K-steps (int8 +1.5%, fp16 +2%).
   constexpr bool kNtC = KIND != KIND_I4 && KIND != KIND_I8_MOD;
-  // ... and pins one MFMA in front of each of a K-step's loads (8192^3 on one
-  // box: int8 2306 against 2271 TOP/s, fp16 1221 against 1182 TFLOP/s),
+  // ... and pins one MFMA in front of each of a K-step's loads (8192^3, one
+  // MI355X: int8 2306 against 2271 TOP/s, fp16 1221 against 1182 TFLOP/s),
   // except for int4, whose expanded operands would then spill
   constexpr bool kPinLoads = KIND != KIND_I4;
 

@@ -30,7 +30,7 @@ F16_TOL = 1e-3
 def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    lp.load_library()          # a GPU box without the built library fails here, loudly
+    lp.load_library()          # a GPU machine without the built library fails here, loudly
 
 
 def _say(*a):

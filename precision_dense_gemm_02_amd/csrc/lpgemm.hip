@@ -134,7 +134,8 @@ enum KernelCfg {
   CFG_256_S2_R128_PIN_L1 = 42,   // configuration 0 with all of a stage's loads pinned in K-step 0
   CFG_256_S2_R128_PIN_L3 = 43,   // configuration 0 with the loads pinned over K-steps 0-2
   CFG_256_S2_R128_PIN_I4 = 44,   // configuration 0 with pinned loads also for int4
-  CFG_COUNT = 45
+  CFG_256_S2_R128_PIN_E3M2 = 45, // E3M2 on configuration 0 with one MFMA pinned in front of each load
+  CFG_COUNT = 46
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -166,7 +167,7 @@ int forced_config() {
 // rows (two 64-value MFMA steps per stage); the reduced int8 kind of the
 // fp64 emulation uses the same three.
 bool supports_e3m2(int c) {
-  return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128;
+  return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128 || c == CFG_256_S2_R128_PIN_E3M2;
 }
 
 KernelCfg choose_config_e3m2(int64_t M, int64_t N, int cu_count) {
@@ -180,6 +181,8 @@ KernelCfg choose_config_e3m2(int64_t M, int64_t N, int cu_count) {
 
 KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   const int f = forced_config();
+  // configuration 45 differs from 0 only for the E3M2 kind
+  if (f == CFG_256_S2_R128_PIN_E3M2) return CFG_256_S2_R128;
   if (f >= 0) return (KernelCfg)f;
   const bool int8_rows = kind == KIND_I8 || kind == KIND_I8_DEQUANT;
   // few rows against many columns: stream B with split-K workgroups
@@ -289,6 +292,10 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     }
   } else if constexpr (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) {
     switch (cfg) {
+      case CFG_256_S2_R128_PIN_E3M2:
+        return launch<256, 256>(
+            (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 0, kNtC, 0, false, true>, args, 256,
+            stream);
       case CFG_256_S2_R128:
         return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 0, kNtC>, args,
                                 256, stream);

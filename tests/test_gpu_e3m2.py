@@ -16,7 +16,7 @@ from precision_dense_gemm_02_amd import inputs  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-E3M2_CONFIGS = (0, 20, 22)   # the kernel configurations that run the E3M2 kind
+E3M2_CONFIGS = (0, 20, 22, 45)   # the kernel configurations that run the E3M2 kind
 
 
 @pytest.fixture(scope="module", autouse=True)

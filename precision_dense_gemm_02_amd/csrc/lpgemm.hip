@@ -417,8 +417,13 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
                               stream);
     case CFG_256_S2_R128_LALL:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
-    default:
+    case CFG_V1_64x64:
       return launch<64, 64>((const void*)&gemm_tiled<KIND, 64, 64, 2, 2>, args, 256, stream);
+    default:
+      // every configuration the choosers can return has a case above; the
+      // stage count was derived from the configuration, so no other kernel
+      // may stand in for one
+      return LPGEMM_ERROR_INVALID_VALUE;
   }
   }
 }

@@ -135,7 +135,8 @@ enum KernelCfg {
   CFG_256_S2_R128_PIN_L3 = 43,   // configuration 0 with the loads pinned over K-steps 0-2
   CFG_256_S2_R128_PIN_I4 = 44,   // configuration 0 with pinned loads also for int4
   CFG_256_S2_R128_PIN_E3M2 = 45, // E3M2 on configuration 0 with one MFMA pinned in front of each load
-  CFG_COUNT = 46
+  CFG_256_S2_R128_PIN_KXN = 46,  // K x N B on configuration 0 with one MFMA pinned in front of each load
+  CFG_COUNT = 47
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -181,8 +182,9 @@ KernelCfg choose_config_e3m2(int64_t M, int64_t N, int cu_count) {
 
 KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   const int f = forced_config();
-  // configuration 45 differs from 0 only for the E3M2 kind
-  if (f == CFG_256_S2_R128_PIN_E3M2) return CFG_256_S2_R128;
+  // configurations 45 and 46 differ from 0 only for the E3M2 kind and for
+  // K x N B
+  if (f == CFG_256_S2_R128_PIN_E3M2 || f == CFG_256_S2_R128_PIN_KXN) return CFG_256_S2_R128;
   if (f >= 0) return (KernelCfg)f;
   const bool int8_rows = kind == KIND_I8 || kind == KIND_I8_DEQUANT;
   // few rows against many columns: stream B with split-K workgroups
@@ -217,7 +219,7 @@ lpgemm_status launch(const void* fn, GemmArgs args, int threads, hipStream_t str
 // B stored K x N row-major runs on the LDS-pipelined kernels with 128-byte
 // stage rows: 128 k-rows of B per stage.
 bool supports_kxn(int c) {
-  return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128;
+  return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128 || c == CFG_256_S2_R128_PIN_KXN;
 }
 
 KernelCfg choose_config_kxn(int64_t M, int64_t N, int cu_count) {
@@ -280,6 +282,10 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
 
   if constexpr (BKN) {
     switch (cfg) {
+      case CFG_256_S2_R128_PIN_KXN:
+        return launch<256, 256>(
+            (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, true, 2, true, 0, false, true>, args, 256,
+            stream);
       case CFG_256_S2_R128:
         return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, true, 2, true>, args,
                                 256, stream);

@@ -13,7 +13,7 @@ from precision_dense_gemm_02_amd import inputs  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = range(46)
+CONFIGS = range(47)
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -15,7 +15,7 @@ from precision_dense_gemm_02_amd import inputs  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-KXN_CONFIGS = (0, 20, 22)   # the configurations that run the K x N layout
+KXN_CONFIGS = (0, 20, 22, 46)   # the configurations that run the K x N layout
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -4,23 +4,33 @@
 A step is one GEMM over one batch of synthetic inputs already resident in
 HBM.  The headline workload is the INT8 square GEMM at M = N = K = 8192 (A
 row-major, B K-contiguous, int32 C); the INT4 and FP16 GEMMs at 8192 are timed
-in the same run and reported under "also".  Prints one JSON line.
+the same way in the same run, and every other configured workload (the square
+sweeps N = 512 ... 4096 and the quantised LLM projection at M = 16, 128,
+2048) follows as a graph-timed sweep entry.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload i8-8192]
-                    [--also i4-8192,f16-8192] [--cpu-seconds S]
+    python bench.py [--steps K] [--warmup W] [--settle-seconds S]
+                    [--workload i8-8192] [--also i4-8192,f16-8192]
+                    [--sweep ...] [--cpu-seconds S]
 
-Timing: W untimed launches (by default enough to reach the steady, power-limited
-clock), then K launches on the current stream bracketed by device
-synchronisations; ms_per_step is the whole timed region / K, and the
-roofline uses the average kernel duration from an event pair around each
-launch on that same stream.  The output of the last timed launch is checked
-against the CPU oracle on sampled rows.  For the HBM-bound LLM shapes the
-weight operand rotates over enough copies (>= 336 MiB) that the 256 MiB
-Infinity Cache cannot hold them.
+Timing of each workload: first a settle phase of back-to-back launches for
+S seconds of wall time (default 1 s; the board needs about that long under
+sustained load to reach its steady, power-limited clock, and the phase also
+touches every input and output page), recorded as `settle_s` and
+`settle_launches`; then W untimed warm-up launches; then K timed launches on
+the current stream bracketed by device synchronisations.  ms_per_step is the
+whole timed region / K, and the roofline uses the average kernel duration
+from an event pair around each launch on that same stream.  Sweep entries
+capture their K launches in one HIP graph and time its replay instead (GPU
+time without the host's per-call overhead, which dominates below about
+20 us per GEMM).  The output of the last timed launch is checked against
+the CPU oracle on sampled rows.  For the HBM-bound LLM shapes the weight
+operand rotates over enough copies (>= 336 MiB) that the 256 MiB Infinity
+Cache cannot hold them.
 
 cpu_baseline: the CPU oracle (plain OpenMP loops) timed on this host on a
 bounded sample of the headline workload (a subset of output rows, sized to
-about --cpu-seconds of work), scaled to the metric's unit.
+about --cpu-seconds of work), scaled to the metric's unit; each sweep entry
+carries its own, sized to about --sweep-cpu-seconds.
 """
 from __future__ import annotations
 
@@ -46,7 +56,12 @@ UNIT = {"i8": "TOPS", "i4": "TOPS", "dq": "TOPS", "w8": "TOPS", "w8f": "TOPS", "
 DTYPE = {"i8": "i8", "i4": "i4", "dq": "i8", "w8": "i8", "w8f": "i8", "f16": "f16", "i4e": "i4", "i4g": "i4",
          "i8kn": "i8", "f64e": "f64"}
 KERNEL_SOURCES = ["precision_dense_gemm_02_amd/csrc/gemm_kernels.hpp",
+                  "precision_dense_gemm_02_amd/csrc/dispatch.hpp",
+                  "precision_dense_gemm_02_amd/csrc/run_kernels.hpp",
                   "precision_dense_gemm_02_amd/csrc/lpgemm.hip"]
+# the square sweeps and LLM shapes measured after the 8192 workloads
+DEFAULT_SWEEP = ("i8-512,i8-1024,i8-2048,i8-4096,i4-512,i4-2048,f16-512,f16-2048,f16-4096,"
+                 "llm-16,llm-128,llm-2048")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -248,10 +263,28 @@ class Workload:
         return f"bit-exact over {len(rows)} sampled rows" if ok else "FAIL"
 
 
-def time_graph(w: Workload, steps: int, warmup: int) -> dict:
+def settle(launch, seconds: float) -> dict:
+    """Run `launch(i)` back to back for about `seconds` of wall time (at least
+    three calls), synchronising once every 8 calls so the host never runs far
+    ahead of the GPU; returns the number of calls and the time taken."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        launch(n)
+        n += 1
+        if n % 8 == 0 or n < 3:
+            torch.cuda.synchronize()
+            if n >= 3 and time.perf_counter() - t0 >= seconds:
+                break
+    torch.cuda.synchronize()
+    return {"settle_launches": n, "settle_s": round(time.perf_counter() - t0, 3)}
+
+
+def time_graph(w: Workload, steps: int, warmup: int, settle_s: float) -> dict:
     """Capture `steps` launches in one HIP graph and time its replay: GPU time
     only, without the host's per-call overhead (which dominates below about
-    20 us per GEMM)."""
+    20 us per GEMM).  The settle phase replays the graph."""
     import torch
     for i in range(max(warmup, 3)):
         w.launch(i)
@@ -260,9 +293,8 @@ def time_graph(w: Workload, steps: int, warmup: int) -> dict:
     with torch.cuda.graph(g):
         for i in range(steps):
             w.launch(i)
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
+    st = settle(lambda i: g.replay(), settle_s)
+    st["settle_launches"] *= steps
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -271,12 +303,13 @@ def time_graph(w: Workload, steps: int, warmup: int) -> dict:
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    return {"ms_per_step": ms, "kernel_ms_avg": ms, "kernel_ms_min": ms, "kernel_ms_median": ms}
+    return {"ms_per_step": ms, "kernel_ms_avg": ms, "kernel_ms_min": ms, "kernel_ms_median": ms, **st}
 
 
-def time_workload(w: Workload, steps: int, warmup: int) -> dict:
+def time_workload(w: Workload, steps: int, warmup: int, settle_s: float) -> dict:
     import torch
     stream = torch.cuda.current_stream()
+    st = settle(w.launch, settle_s)
     for i in range(warmup):
         w.launch(i)
     torch.cuda.synchronize()
@@ -297,7 +330,7 @@ def time_workload(w: Workload, steps: int, warmup: int) -> dict:
     return {"ms_per_step": total_ms / steps,
             "kernel_ms_avg": sum(per) / len(per),
             "kernel_ms_min": per[0],
-            "kernel_ms_median": per[len(per) // 2]}
+            "kernel_ms_median": per[len(per) // 2], **st}
 
 
 def roofline(w: Workload, t: dict) -> dict:
@@ -397,9 +430,9 @@ def f64e_report(w, steps: int, warmup: int) -> dict:
                               "how": "torch.matmul on float64 (the platform library)"}}
 
 
-def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
+def measure(name: str, steps: int, warmup: int, graph: bool = False, settle_s: float = 1.0) -> tuple:
     w = Workload(name)
-    t = time_graph(w, steps, warmup) if graph else time_workload(w, steps, warmup)
+    t = time_graph(w, steps, warmup, settle_s) if graph else time_workload(w, steps, warmup, settle_s)
     r = roofline(w, t)
     value = w.ops / (t["ms_per_step"] / 1e3) / 1e12
     rec = {"workload": name, "value": round(value, 1), "unit": UNIT[w.kind],
@@ -408,6 +441,7 @@ def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
            "kernel_ms_avg": round(t["kernel_ms_avg"], 5),
            "kernel_ms_min": round(t["kernel_ms_min"], 5),
            "pct_mfma_peak": round(100 * value / PEAK_TOPS[w.kind], 2),
+           "settle_s": t["settle_s"], "settle_launches": t["settle_launches"],
            "roofline": r, "parity": w.check_sampled()}
     if w.kind == "w8":
         rec["note"] = ("one step is two launches (per-row quantise, then the dequantising "
@@ -426,7 +460,7 @@ def measure(name: str, steps: int, warmup: int, graph: bool = False) -> tuple:
     return w, rec
 
 
-def platform_library(steps: int, warmup: int, n: int = 8192) -> list:
+def platform_library(steps: int, warmup: int, settle_s: float, n: int = 8192) -> list:
     """torch's own GEMMs on this GPU (hipBLASLt under ROCm) at n^3, timed with
     the same steady-state protocol as the headline: context for the measured
     fraction of peak, not the target.  Operand layouts are the library's:
@@ -439,6 +473,7 @@ def platform_library(steps: int, warmup: int, n: int = 8192) -> list:
     out = []
 
     def timed(fn):
+        settle(lambda i: fn(), settle_s)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -469,11 +504,12 @@ def platform_library(steps: int, warmup: int, n: int = 8192) -> list:
     return out
 
 
-# the kernel each square workload runs at 8192 (configuration 0)
+# the kernel each square workload runs at 8192 (the persistent configuration
+# 47 for int8 and fp16, configuration 0 for int4)
 TRAFFIC_KERNELS = {
-    "i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true>(lpgemm::GemmArgs)",
-    "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false>(lpgemm::GemmArgs)",
-    "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true>(lpgemm::GemmArgs)"}
+    "i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true>(lpgemm::GemmArgs)",
+    "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false, false>(lpgemm::GemmArgs)",
+    "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true>(lpgemm::GemmArgs)"}
 
 
 def _median_counter(path: str, kernel: str, counter: str) -> float:
@@ -514,11 +550,21 @@ def main():
     # The board settles at its power limit within about half a second of
     # sustained load (the clock drops well below its 2.4 GHz maximum), so the
     # default warm-up runs long enough to time the steady state.
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=1500)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="wall time of back-to-back launches before the warm-up of each workload "
+                         "(reported as settle_s / settle_launches)")
     ap.add_argument("--workload", default="i8-8192")
     ap.add_argument("--also", default="i4-8192,f16-8192",
-                    help="comma-separated extra workloads timed in the same run ('' for none)")
+                    help="comma-separated extra workloads timed like the headline ('' for none)")
+    ap.add_argument("--sweep", default=DEFAULT_SWEEP,
+                    help="comma-separated workloads timed as graph replays after the others, each "
+                         "with its own sampled CPU-oracle time ('' for none)")
+    ap.add_argument("--sweep-steps", type=int, default=100,
+                    help="launches per captured graph of a sweep entry")
+    ap.add_argument("--sweep-settle-seconds", type=float, default=0.3)
+    ap.add_argument("--sweep-cpu-seconds", type=float, default=1.0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as one captured HIP graph (GPU time without host "
@@ -563,15 +609,25 @@ def main():
     import precision_dense_gemm_02_amd as lp
     lp.load_library()
 
-    w, head = measure(args.workload, args.steps, args.warmup, args.graph)
+    w, head = measure(args.workload, args.steps, args.warmup, args.graph, args.settle_seconds)
     print(f"# {head['workload']}: {head['value']} {head['unit']} ({head['parity']})",
           file=sys.stderr, flush=True)
     also = []
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
-        _, rec = measure(name, args.steps, args.warmup, args.graph)
+        _, rec = measure(name, args.steps, args.warmup, args.graph, args.settle_seconds)
         print(f"# {rec['workload']}: {rec['value']} {rec['unit']} ({rec['parity']})",
               file=sys.stderr, flush=True)
         also.append(rec)
+    done = {args.workload, *[r["workload"] for r in also]}
+    for name in [s for s in args.sweep.split(",") if s and s not in done]:
+        sw, rec = measure(name, args.sweep_steps, args.warmup, True, args.sweep_settle_seconds)
+        if not args.no_cpu_baseline:
+            rec["cpu_baseline"] = cpu_baseline(sw, args.sweep_cpu_seconds)
+        print(f"# sweep {rec['workload']}: {rec['value']} {rec['unit']}, roofline "
+              f"{rec['roofline']['frac']} of {rec['roofline']['bound']} ({rec['parity']})",
+              file=sys.stderr, flush=True)
+        also.append(rec)
+        del sw
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -580,13 +636,14 @@ def main():
 
     platform = None
     if not args.no_platform and not args.graph and args.workload == "i8-8192":
-        platform = platform_library(args.steps, args.warmup)
+        platform = platform_library(args.steps, args.warmup, args.settle_seconds)
         for r in platform:
             print(f"# platform library: {r}", file=sys.stderr, flush=True)
 
     line = {
         "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "steps": args.steps, "warmup": args.warmup, "settle_s": head["settle_s"],
+        "settle_launches": head["settle_launches"], "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": DTYPE[w.kind], "data": "synthetic",
         "config": {"workload": head["workload"], "M": w.M, "N": w.N, "K": w.K, "seed": w.seed,

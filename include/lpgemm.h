@@ -207,6 +207,22 @@ const char *lpgemm_status_string(lpgemm_status status);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int lpgemm_version(void);
 
+/* Ablation hook (the PTX-vs-WMMA summary page varies one kernel knob at a
+ * time around its best kernel; this makes the same walk possible here).
+ * lpgemm_config_count() is the number of kernel configurations the GEMM
+ * entry points know.  lpgemm_force_config(c) pins configuration c
+ * (0 <= c < lpgemm_config_count()) for every later GEMM call in the process,
+ * or restores the automatic choice per shape for any other value (-1); it
+ * returns the previous setting (-1 = automatic).  A configuration that an
+ * entry point cannot run (for instance one without 128-byte stage rows for
+ * lpgemm_i4_e3m2) leaves that entry point on its automatic choice.  The
+ * environment variable LPGEMM_FORCE_CONFIG sets the initial value when the
+ * library loads.  The setting is process-wide and not synchronised with
+ * calls in flight on other host threads; results do not depend on it (every
+ * configuration computes the same C), only the speed does. */
+int lpgemm_config_count(void);
+int lpgemm_force_config(int config);
+
 #ifdef __cplusplus
 }
 #endif

@@ -79,6 +79,10 @@ def load_library():
         lib.lpgemm_status_string.restype = ctypes.c_char_p
         lib.lpgemm_version.argtypes = []
         lib.lpgemm_version.restype = ctypes.c_int
+        lib.lpgemm_config_count.argtypes = []
+        lib.lpgemm_config_count.restype = ctypes.c_int
+        lib.lpgemm_force_config.argtypes = [ctypes.c_int]
+        lib.lpgemm_force_config.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -99,6 +103,17 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return int(load_library().lpgemm_version())
+
+
+def config_count() -> int:
+    """Number of kernel configurations the GEMM entry points know."""
+    return int(load_library().lpgemm_config_count())
+
+
+def force_config(config: int) -> int:
+    """Pin kernel configuration `config` for later GEMM calls in this process
+    (-1: automatic choice per shape); returns the previous setting."""
+    return int(load_library().lpgemm_force_config(int(config)))
 
 
 def _check(status: int, what: str) -> None:

@@ -1,0 +1,250 @@
+// Host-side dispatch shared by the translation units of liblpgemm: argument
+// checks, the kernel configurations and their choice per shape, and the
+// launch of one GEMM kernel (run<KIND, BKN>).
+//
+// run<> is defined here and instantiated once per operand kind in its own
+// translation unit (run_*.hip), so that the library's kernel instantiations
+// compile in parallel; lpgemm.hip, which holds the C entry points, sees only
+// the declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "../../include/lpgemm.h"
+#include "gemm_kernels.hpp"
+
+namespace lpgemm {
+
+struct DeviceInfo {
+  bool probed = false;
+  bool is_gfx950 = false;
+  int cu_count = 0;
+};
+
+// Current device's properties, read once per device (lpgemm.hip).
+lpgemm_status current_device(DeviceInfo& out);
+
+// The configuration pinned by lpgemm_force_config (or LPGEMM_FORCE_CONFIG at
+// load time), -1 for automatic selection (lpgemm.hip).
+extern std::atomic<int> g_forced_config;
+inline int forced_config() { return g_forced_config.load(std::memory_order_relaxed); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Host-only argument checks, in the order the header documents.  Sets
+// `nothing_to_do` when the product is empty (M or N is zero).
+inline lpgemm_status validate(Kind kind, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                              const void* C, const void* rs, const void* cs, bool& nothing_to_do) {
+  nothing_to_do = false;
+  if (M < 0 || N < 0 || K < 0) return LPGEMM_ERROR_INVALID_VALUE;
+  if (M > INT32_MAX || N > INT32_MAX) return LPGEMM_ERROR_INVALID_VALUE;
+  switch (kind) {
+    case KIND_I8:
+    case KIND_I8_DEQUANT:
+    case KIND_I8_MOD:
+      if (K % 16 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+      break;
+    case KIND_I4:
+    case KIND_I4_E3M2:
+      if (K % 32 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+      break;
+    case KIND_F16:
+      if (K % 8 != 0 || K > LPGEMM_MAX_K_F16) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+      break;
+  }
+  if (M == 0 || N == 0) {
+    nothing_to_do = true;
+    return LPGEMM_SUCCESS;
+  }
+  if (!C) return LPGEMM_ERROR_INVALID_VALUE;
+  if (K > 0 && (!A || !B)) return LPGEMM_ERROR_INVALID_VALUE;
+  if (kind == KIND_I8_DEQUANT && (!rs || !cs)) return LPGEMM_ERROR_INVALID_VALUE;
+  if (!aligned16(C)) return LPGEMM_ERROR_MISALIGNED;
+  if (K > 0 && (!aligned16(A) || !aligned16(B))) return LPGEMM_ERROR_MISALIGNED;
+  if (kind == KIND_I8_DEQUANT && (!aligned4(rs) || !aligned4(cs))) return LPGEMM_ERROR_MISALIGNED;
+  return LPGEMM_SUCCESS;
+}
+
+// Kernel configurations.  The four-wave direct-to-LDS kernel with 256 x 256
+// tiles has the best operand reuse; smaller tiles fill the 256 CUs when the
+// product has few 256 x 256 tiles.
+enum KernelCfg {
+  CFG_256_S2_R128 = 0,   // 4 waves, 256 x 256, 2 stages of 128-byte rows (see kNtC)
+  CFG_256_S4_R64 = 1,    // 4 waves, 256 x 256, 4 stages of 64-byte rows
+  CFG_256_S3_R64 = 2,    // 4 waves, 256 x 256, 3 stages of 64-byte rows
+  CFG_128_S4_R64 = 3,    // 4 waves, 128 x 128, 4 stages of 64-byte rows
+  CFG_V1_256x256 = 4,    // 8 waves, 128 x 64 per wave, register-staged loads
+  CFG_V1_128x128 = 5,    // 4 waves, 64 x 64 per wave, register-staged loads
+  CFG_V1_64x64 = 6,      // 4 waves, 32 x 32 per wave, register-staged loads
+  CFG_PP_R64 = 7,        // 8 waves ping-pong, 256 x 256, 4 stages of 64-byte rows
+  CFG_SKINNY_32 = 8,     // 32 x 32 tiles, 8 waves split K, 4 K-blocks per load round
+  CFG_SKINNY_64 = 9,     // 64 x 32 tiles, 8 waves split K, 2 K-blocks per load round
+  CFG_SKINNY_32_W16 = 10,  // 32 x 32 tiles, 16 waves split K, 2 K-blocks per load round
+  CFG_SKINNY_LDS_R2 = 11,  // 32 x 32 tiles, 8 waves split K, B through LDS, 2 K-blocks per round
+  CFG_SKINNY_LDS_R4 = 12,  // 32 x 32 tiles, 8 waves split K, B through LDS, 4 K-blocks per round
+  CFG_SKINNY_LDS_W4 = 13,  // 32 x 32 tiles, 4 waves split K, B through LDS, 4 K-blocks per round
+  CFG_SKINNY_PIPE_W4R2 = 14,  // as 13, double-buffered rounds of 2 K-blocks
+  CFG_SKINNY_PIPE_W8R1 = 15,  // 8 waves, double-buffered rounds of 1 K-block
+  CFG_SKINNY_PIPE_W4R3 = 16,  // 4 waves, double-buffered rounds of 3 K-blocks
+  CFG_SKINNY_PIPE_W8R2 = 17,  // 8 waves, double-buffered rounds of 2 K-blocks
+  CFG_128x64_S4_R64 = 18,     // 4 waves, 128 x 64, 4 stages of 64-byte rows
+  CFG_256x128_S4_R64 = 19,    // 4 waves, 256 x 128, 4 stages of 64-byte rows
+  CFG_128x64_S6_R128 = 20,    // 4 waves, 128 x 64, 6 stages of 128-byte rows
+  CFG_128x64_S8_R64 = 21,     // 4 waves, 128 x 64, 8 stages of 64-byte rows
+  CFG_128_S4_R128 = 22,       // 4 waves, 128 x 128, 4 stages of 128-byte rows
+  // ablations of configuration 0
+  CFG_256_S2_R128_NT = 23,       // operand loads non-temporal (nt)
+  CFG_256_S2_R128_SC0 = 24,      // operand loads sc0
+  CFG_256_S2_R128_SC01 = 25,     // operand loads sc0 sc1
+  CFG_256_S2_R128_SPLIT = 26,    // split loader: two waves load A, two load B
+  CFG_256_S2_R128_L1 = 27,       // the next stage's loads all issued in K-step 0
+  CFG_256_S2_R128_LALL = 28,     // ... spread over all K-steps but the last
+  CFG_256_S2_R128_CACHED_C = 29, // C written with ordinary (cached) stores
+  CFG_256_S2_R128_B4 = 30,       // stage barrier after 4 of the last K-step's 16 MFMAs
+  CFG_256_S2_R128_B12 = 31,      // ... after 12
+  CFG_256_S5_R64_NT = 32,        // 4 waves, 256 x 256, 5 stages of 64-byte rows (all 160 KiB), NT C
+  CFG_256_S4_R64_NT = 33,        // 4 waves, 256 x 256, 4 stages of 64-byte rows, NT C
+  CFG_128x64_S3_R256 = 34,       // 4 waves, 128 x 64, 3 stages of 256-byte rows
+  CFG_128_S5_R128 = 35,          // 4 waves, 128 x 128, 5 stages of 128-byte rows (all 160 KiB)
+  CFG_128_S2_R256 = 36,          // 4 waves, 128 x 128, 2 stages of 256-byte rows
+  CFG_256_S2_R128_PF = 37,       // configuration 0 plus an L2 prefetch of the stage after next
+  CFG_256_S2_R128_SCHED = 38,    // configuration 0 with the loads placed by the compiler's schedule
+  CFG_128_S2_R256_PIN = 39,      // configuration 36 with one MFMA pinned in front of each load
+  CFG_128_S4_R128_PIN = 40,      // configuration 22 with one MFMA pinned in front of each load
+  CFG_128x64_S3_R256_PIN = 41,   // configuration 34 with one MFMA pinned in front of each load
+  CFG_256_S2_R128_PIN_L1 = 42,   // configuration 0 with all of a stage's loads pinned in K-step 0
+  CFG_256_S2_R128_PIN_L3 = 43,   // configuration 0 with the loads pinned over K-steps 0-2
+  CFG_256_S2_R128_PIN_I4 = 44,   // configuration 0 with pinned loads also for int4
+  CFG_256_S2_R128_PIN_E3M2 = 45, // E3M2 on configuration 0 with one MFMA pinned in front of each load
+  CFG_256_S2_R128_PIN_KXN = 46,  // K x N B on configuration 0 with one MFMA pinned in front of each load
+  CFG_256_S2_R128_PERSIST = 47,  // configuration 0 as a persistent grid of at most one workgroup per CU
+  CFG_COUNT = 48
+};
+
+// Row bytes of one LDS K-stage for a configuration (the register-staged
+// kernels expand int4 to int8 on the way into LDS, 128 values per stage).
+inline int stage_row_bytes(KernelCfg c) {
+  return (c == CFG_256_S4_R64 || c == CFG_256_S3_R64 || c == CFG_128_S4_R64 || c == CFG_PP_R64 ||
+          c == CFG_128x64_S4_R64 || c == CFG_256x128_S4_R64 || c == CFG_128x64_S8_R64 ||
+          c == CFG_256_S5_R64_NT || c == CFG_256_S4_R64_NT)
+             ? 64
+             : ((c == CFG_128x64_S3_R256 || c == CFG_128_S2_R256) ? 256 : 128);
+}
+inline bool expands_int4_in_lds(KernelCfg c) { return c >= CFG_V1_256x256 && c <= CFG_V1_64x64; }
+
+inline int tiles(int64_t x, int t) { return (int)((x + t - 1) / t); }
+
+// The E3M2 kind runs only on the LDS-pipelined kernels with 128-byte stage
+// rows (two 64-value MFMA steps per stage); the reduced int8 kind of the
+// fp64 emulation uses the same three.
+inline bool supports_e3m2(int c) {
+  return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128 || c == CFG_256_S2_R128_PIN_E3M2;
+}
+
+inline KernelCfg choose_config_e3m2(int64_t M, int64_t N, int cu_count) {
+  const int f = forced_config();
+  if (f >= 0 && supports_e3m2(f)) return (KernelCfg)f;
+  if (M <= 128) return CFG_128x64_S6_R128;
+  if ((int64_t)tiles(M, 256) * tiles(N, 256) >= cu_count) return CFG_256_S2_R128;
+  if ((int64_t)tiles(M, 128) * tiles(N, 128) >= cu_count / 2) return CFG_128_S4_R128;
+  return CFG_128x64_S6_R128;
+}
+
+inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
+  const int f = forced_config();
+  // configurations 45 and 46 differ from 0 only for the E3M2 kind and for
+  // K x N B
+  if (f == CFG_256_S2_R128_PIN_E3M2 || f == CFG_256_S2_R128_PIN_KXN) return CFG_256_S2_R128;
+  if (f >= 0) return (KernelCfg)f;
+  const bool int8_rows = kind == KIND_I8 || kind == KIND_I8_DEQUANT;
+  // few rows against many columns: stream B with split-K workgroups
+  if (M <= 32) return CFG_SKINNY_PIPE_W4R2;
+  if (M <= 64) return CFG_SKINNY_64;
+  // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128.
+  // int8 rows stream B in 256-byte pieces per stage (M = 128, K = 4096,
+  // N = 14336: 19.2 us against 20.4 us with six 128-byte stages)
+  if (M <= 128) return int8_rows ? CFG_128x64_S3_R256 : CFG_128x64_S6_R128;
+  const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
+  // two or more full rounds of 256 x 256 tiles: the persistent grid, whose
+  // workgroups load a tile's first stage while they store the previous
+  // tile's C (8192^3: int8 +3.0%, fp16 +1.6%); int4 stays on configuration
+  // 0, whose registers leave no room for the persistent state
+  if (big >= 2 * (int64_t)cu_count && kind != KIND_I4) return CFG_256_S2_R128_PERSIST;
+  if (big >= cu_count) return CFG_256_S2_R128;
+  // 128 x 128 tiles: at 2048^3, two 256-byte stages for int8 and int4
+  // (14.5 / 15.0 us against 15.4 / 15.7 us with four 64-byte stages), four
+  // 128-byte stages for fp16 (23.1 against 25.4 us)
+  const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
+  if (mid >= cu_count / 2) return kind == KIND_F16 ? CFG_128_S4_R128 : CFG_128_S2_R256;
+  return CFG_V1_64x64;
+}
+
+// B stored K x N row-major runs on the LDS-pipelined kernels with 128-byte
+// stage rows: 128 k-rows of B per stage.
+inline bool supports_kxn(int c) {
+  return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128 || c == CFG_256_S2_R128_PIN_KXN;
+}
+
+inline KernelCfg choose_config_kxn(int64_t M, int64_t N, int cu_count) {
+  const int f = forced_config();
+  if (f >= 0 && supports_kxn(f)) return (KernelCfg)f;
+  if (M <= 128) return CFG_128x64_S6_R128;
+  if ((int64_t)tiles(M, 256) * tiles(N, 256) >= cu_count) return CFG_256_S2_R128;
+  if ((int64_t)tiles(M, 128) * tiles(N, 128) >= cu_count / 2) return CFG_128_S4_R128;
+  return CFG_128x64_S6_R128;
+}
+
+template <int BM, int BN>
+lpgemm_status launch(const void* fn, GemmArgs args, int threads, hipStream_t stream) {
+  args.tiles_m = tiles(args.M, BM);
+  args.tiles_n = tiles(args.N, BN);
+  args.group_m = 8;
+  const int64_t nblocks = (int64_t)args.tiles_m * args.tiles_n;
+  if (nblocks > INT32_MAX) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  void* kargs[] = {&args};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(threads), kargs, 0, stream);
+  return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
+}
+
+// A persistent launch: at most `max_groups` workgroups (one per CU), each
+// walking its tiles round by round (gemm_v3<..., PERSIST = true>).
+template <int BM, int BN>
+lpgemm_status launch_persistent(const void* fn, GemmArgs args, int threads, hipStream_t stream, int max_groups) {
+  args.tiles_m = tiles(args.M, BM);
+  args.tiles_n = tiles(args.N, BN);
+  args.group_m = 8;
+  const int64_t ntiles = (int64_t)args.tiles_m * args.tiles_n;
+  if (ntiles > INT32_MAX - (int64_t)max_groups) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  const int64_t groups = ntiles < max_groups ? ntiles : max_groups;
+  void* kargs[] = {&args};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(groups > 0 ? groups : 1)), dim3(threads), kargs, 0, stream);
+  return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
+}
+
+// One GEMM of the given kind (BKN: B stored K x N) on `stream`: validation,
+// the configuration for the shape, and the kernel launch.  Defined in
+// run_kernels.hpp; instantiated in run_*.hip.
+template <int KIND, bool BKN = false>
+lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, const float* rs,
+                  const float* cs, hipStream_t stream, int modulus = 0);
+
+extern template lpgemm_status run<KIND_I8, false>(int64_t, int64_t, int64_t, const void*, const void*, void*,
+                                                  const float*, const float*, hipStream_t, int);
+extern template lpgemm_status run<KIND_I4, false>(int64_t, int64_t, int64_t, const void*, const void*, void*,
+                                                  const float*, const float*, hipStream_t, int);
+extern template lpgemm_status run<KIND_F16, false>(int64_t, int64_t, int64_t, const void*, const void*, void*,
+                                                   const float*, const float*, hipStream_t, int);
+extern template lpgemm_status run<KIND_I8_DEQUANT, false>(int64_t, int64_t, int64_t, const void*, const void*,
+                                                          void*, const float*, const float*, hipStream_t, int);
+extern template lpgemm_status run<KIND_I4_E3M2, false>(int64_t, int64_t, int64_t, const void*, const void*,
+                                                       void*, const float*, const float*, hipStream_t, int);
+extern template lpgemm_status run<KIND_I8_MOD, false>(int64_t, int64_t, int64_t, const void*, const void*,
+                                                      void*, const float*, const float*, hipStream_t, int);
+extern template lpgemm_status run<KIND_I8, true>(int64_t, int64_t, int64_t, const void*, const void*, void*,
+                                                 const float*, const float*, hipStream_t, int);
+
+}  // namespace lpgemm

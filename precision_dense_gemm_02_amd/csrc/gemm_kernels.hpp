@@ -88,12 +88,28 @@ __device__ __forceinline__ int lds_offset(int r, int c) {
 // XCD a contiguous range of logical tile ids, then walk those ids in groups
 // of `group_m` tile rows so that workgroups resident together on one XCD
 // share A row panels and B column panels in that XCD's L2.
+// The logical id of workgroup w in a grid of nb workgroups.
+__device__ __forceinline__ int xcd_logical(int w, int nb) {
+  const int xcd = w & 7;
+  const int q = nb >> 3, rem = nb & 7;
+  return xcd * q + (xcd < rem ? xcd : rem) + (w >> 3);
+}
+
+// (tile_m, tile_n) of a logical tile id.
+__device__ __forceinline__ void tile_of(const GemmArgs& p, int logical, int& tm, int& tn) {
+  const int per_group = p.group_m * p.tiles_n;
+  const int group = logical / per_group;
+  const int first_m = group * p.group_m;
+  const int gm = min(p.tiles_m - first_m, p.group_m);
+  const int in_group = logical - group * per_group;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+}
+
 __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn) {
   const int nb = gridDim.x;
   const int w = blockIdx.x;
-  const int xcd = w & 7;
-  const int q = nb >> 3, rem = nb & 7;
-  const int logical = xcd * q + (xcd < rem ? xcd : rem) + (w >> 3);
+  const int logical = xcd_logical(w, nb);
   const int per_group = p.group_m * p.tiles_n;
   const int group = logical / per_group;
   const int first_m = group * p.group_m;
@@ -543,9 +559,20 @@ struct RowLayout<64> {
 // of every operand row's stage s + STAGES chunk (one 64-row load per 64 rows,
 // into a 256-byte LDS sink), so that the chunk's lines are on their way to
 // the L2 one stage before the real loads ask for them.
+//
+// PERSIST: a persistent grid (at most one workgroup per CU, launched with
+// the number of workgroups in gridDim.x) in which each workgroup walks its
+// tiles round by round, tile r·G + (its logical id) in round r, so that a
+// round covers the same tiles, on the same XCDs, as one wave of a
+// one-tile-per-workgroup launch.  The stage after a tile's last one is the
+// next tile's first: its loads go out during the last stage like any other,
+// so the next tile's operands are on their way while this tile's C is
+// staged and stored, and the next tile's first fragments are read before
+// the epilogue.  The epilogue therefore stages 32 rows per wave at a time
+// and keeps clear of the LDS stage those loads fill.  Two stages only.
 template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false,
           bool BKN = false, int LSTEPS = 0, bool NTC = false, int BSPLIT = 0, bool PF = false,
-          bool HIL = false>
+          bool HIL = false, bool PERSIST = false>
 __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
@@ -575,11 +602,19 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   constexpr int kSlotsA = BM / kRowsPerLoad / 4;
   static_assert((STAGES - 2) * kSlots <= 63, "vmcnt range");
   constexpr int kMainLds = STAGES * kStage;
-  // epilogue staging: per wave 64 rows of WTN 4-byte values plus 32 B padding
+  // epilogue staging: per wave 64 rows (32 when persistent) of WTN 4-byte
+  // values plus 32 B padding
   constexpr int kEpiPitch = WTN * 4 + 32;
-  constexpr int kEpiRows = 64;
-  constexpr int kEpiLds = 4 * kEpiRows * kEpiPitch;
-  constexpr int kLds0 = kMainLds > kEpiLds ? kMainLds : kEpiLds;
+  constexpr int kEpiRows = PERSIST ? 32 : 64;
+  constexpr int kEpiWave = kEpiRows * kEpiPitch;
+  constexpr int kEpiLds = 4 * kEpiWave;
+  static_assert(!PERSIST || (STAGES == 2 && !PF && !BKN && !SPLIT && KIND != KIND_I8_MOD), "persistent variant");
+  // persistent: the epilogue avoids the stage the next tile's first loads
+  // fill.  Stage 0 in flight: the four waves stage in [kStage, kStage +
+  // kEpiLds).  Stage 1 in flight: waves 0-2 stage in stage 0's space, wave 3
+  // past the ring.
+  static_assert(!PERSIST || (3 * kEpiWave <= kStage && kStage + kEpiLds <= kMainLds + kEpiWave), "staging");
+  constexpr int kLds0 = PERSIST ? kMainLds + kEpiWave : (kMainLds > kEpiLds ? kMainLds : kEpiLds);
   // prefetch: 64-row touches per wave per stage, and their LDS sink
   static_assert(!PF || (!BKN && BM % 64 == 0 && (BM + BN) % 256 == 0), "prefetch rows");
   constexpr int kPf = PF ? (BM + BN) / 256 : 0;
@@ -594,16 +629,44 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
+  // this workgroup's (first) tile; persistent: round r takes logical tile
+  // r G + xcd_logical(workgroup)
+  const int ntiles = p.tiles_m * p.tiles_n;
+  int logical = PERSIST ? xcd_logical(blockIdx.x, gridDim.x) : 0;
   int tm, tn;
-  tile_coords(p, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int rows_a = min(BM, p.M - m0);
-  const int rows_b = min(BN, p.N - n0);
-  const i32x4 rsrc_a = make_rsrc(p.A + (size_t)m0 * p.row_bytes, rows_a * p.row_bytes);
+  if constexpr (PERSIST) tile_of(p, logical, tm, tn);
+  else tile_coords(p, tm, tn);
+  int m0 = tm * BM, n0 = tn * BN;
+  // buffer resources over a tile's A and B row panels
+  auto panel_a = [&](int mm0) -> i32x4 {
+    return make_rsrc(p.A + (size_t)mm0 * p.row_bytes, min(BM, p.M - mm0) * p.row_bytes);
+  };
+  auto panel_b = [&](int nn0) -> i32x4 {
+    return make_rsrc(p.B + (size_t)nn0 * p.row_bytes, min(BN, p.N - nn0) * p.row_bytes);
+  };
+  i32x4 rsrc_a = panel_a(m0);
   // K-contiguous B: this tile's BN rows; K x N B: the whole matrix (K rows of
   // N bytes, below 2^31 bytes), columns selected per lane
-  const i32x4 rsrc_b = BKN ? make_rsrc(p.B, (uint32_t)p.row_bytes * (uint32_t)p.N)
-                           : make_rsrc(p.B + (size_t)n0 * p.row_bytes, rows_b * p.row_bytes);
+  i32x4 rsrc_b = BKN ? make_rsrc(p.B, (uint32_t)p.row_bytes * (uint32_t)p.N) : panel_b(n0);
+  // persistent: the next tile's panels (empty resources, which read as
+  // zero, after the last tile)
+  int logical_next = logical + (int)gridDim.x;
+  i32x4 rsrc_a_next = rsrc_a, rsrc_b_next = rsrc_b;
+  auto set_next = [&]() {
+    if (logical_next < ntiles) {
+      int tm2, tn2;
+      tile_of(p, logical_next, tm2, tn2);
+      rsrc_a_next = panel_a(tm2 * BM);
+      rsrc_b_next = panel_b(tn2 * BN);
+    } else {
+      rsrc_a_next = make_rsrc(p.A, 0);
+      rsrc_b_next = make_rsrc(p.B, 0);
+    }
+  };
+  if constexpr (PERSIST) set_next();
+  // parity of the LDS stage holding a tile's first K-stage (persistent: the
+  // stages run on across tiles)
+  int gbase = 0;
   const uint32_t smem_lds = lds_address(smem);
 
   // Load slot t of this wave fills stage rows kRowsPerLoad*g .. (g = 4t +
@@ -647,8 +710,10 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     }
   }
 
+  // stage s of this tile (persistent: s = nks is the next tile's stage 0)
   auto issue_load = [&](int t, int s) {
-    const uint32_t kbyte = (uint32_t)s * ROWB;
+    const bool next = PERSIST && s >= p.k_stages;
+    const uint32_t kbyte = next ? 0u : (uint32_t)s * ROWB;
     const int g = group_of(t);
     uint32_t off;
     if (BKN && !is_a(t)) {
@@ -659,7 +724,9 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       const bool in_row = kbyte + slot_col[t] < (uint32_t)p.row_bytes;
       off = in_row ? slot_off[t] + kbyte : kOutOfRange;
     }
-    lds_dma_16<CPOL>(is_a(t) ? rsrc_a : rsrc_b, smem_lds + (s % STAGES) * kStage + g * 1024, off);
+    const i32x4 ra = next ? rsrc_a_next : rsrc_a;
+    const i32x4 rb = next ? rsrc_b_next : rsrc_b;
+    lds_dma_16<CPOL>(is_a(t) ? ra : rb, smem_lds + ((gbase + s) % STAGES) * kStage + g * 1024, off);
   };
 
   // prefetch touch t of this wave covers operand rows 64 (kPf wave + t) ..
@@ -714,7 +781,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   };
 
   auto read_frags = [&](int s, int kk, int dst) {
-    const uint8_t* base = smem + (s % STAGES) * kStage;
+    const uint8_t* base = smem + ((gbase + s) % STAGES) * kStage;
     const int off = frag_off(kk);
     if constexpr (BKN) {
 #pragma unroll
@@ -817,9 +884,10 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     block_barrier();                             // everyone's
     read_frags(0, 0, 0);
   }
+  for (;;) {   // tiles: one pass, or every round's tile of a persistent workgroup
   for (int s = 0; s < nks; ++s) {
     // loads for stage s + STAGES - 1 (past the last stage they only write
-    // zeros that nobody reads)
+    // zeros that nobody reads, or, persistent, fill the next tile's stage 0)
     const int sl = s + STAGES - 1;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -898,17 +966,27 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
 
   // Outstanding loads (all past the last stage) must land before LDS is
   // reused; the barrier then also covers every wave's fragment reads.
+  // Persistent: the last K-step already waited for every load (the next
+  // tile's stage 0) and its barrier followed every wave's last reads of the
+  // stage the staging reuses; the staging keeps clear of the next tile's
+  // stage 0, which the fragment reads of its first K-step are reading.
   wait_vmcnt<0>();
   wait_lgkmcnt0();
   if constexpr (KIND != KIND_I8_MOD) {
     // Every kind but the reduced one goes through LDS: each wave transposes
-    // 64 rows of its quadrant at a time so that a lane holds 4 consecutive
-    // columns of one row.  A tile inside C whose rows start 16-byte aligned
-    // (N % 4 == 0) writes them with 16-byte stores; an edge tile writes each
-    // value inside C with its own 4-byte store.
+    // kEpiRows rows of its quadrant at a time so that a lane holds 4
+    // consecutive columns of one row.  A tile inside C whose rows start
+    // 16-byte aligned (N % 4 == 0) writes them with 16-byte stores; an edge
+    // tile writes each value inside C with its own 4-byte store.
     const bool full = m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 3) == 0;
-    block_barrier();   // every wave is done with the operand stages
-    uint8_t* stage_out = smem + wave * kEpiRows * kEpiPitch;
+    int stage_off = wave * kEpiWave;
+    if constexpr (PERSIST) {
+      const bool next_in_0 = (gbase + nks) % STAGES == 0;
+      stage_off = next_in_0 ? kStage + wave * kEpiWave : (wave < 3 ? wave * kEpiWave : 2 * kStage);
+    } else {
+      block_barrier();   // every wave is done with the operand stages
+    }
+    uint8_t* stage_out = smem + stage_off;
     const int row0 = m0 + wm * WTM;
     const int col0 = n0 + wn * WTN;
     // each lane stores 16 bytes; lanes 0..WTN/4-1 cover one row
@@ -923,12 +1001,14 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       for (int x = 0; x < 4; ++x)
         if (col0 + c_lane + x < p.N) cs4[x] = p.col_scale[col0 + c_lane + x];
     }
+    constexpr int kBlk = kEpiRows / 32;   // accumulator block rows per pass
 #pragma unroll
-    for (int half = 0; half < TM / 2; ++half) {
-      // accumulator blocks i = 2*half, 2*half+1 cover 64 rows of the quadrant
+    for (int half = 0; half < TM / kBlk; ++half) {
+      // accumulator blocks i = kBlk*half .. + kBlk - 1 cover kEpiRows rows of
+      // the quadrant
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * half + ii;
+      for (int ii = 0; ii < kBlk; ++ii) {
+        const int i = kBlk * half + ii;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -942,12 +1022,12 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
           }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes done
-      // dequant: lane l holds the scale of row l of these 64 (zero outside
-      // C); each store's rows take theirs by lane index
+      // dequant: lane l holds the scale of row l of these kEpiRows (zero
+      // outside C); each store's rows take theirs by lane index
       float rs_half = 0.f;
       if constexpr (KIND == KIND_I8_DEQUANT) {
-        const int rl = row0 + half * 64 + lane;
-        if (rl < p.M) rs_half = p.row_scale[rl];
+        const int rl = row0 + half * kEpiRows + lane;
+        if (lane < kEpiRows && rl < p.M) rs_half = p.row_scale[rl];
       }
 #pragma unroll
       for (int r0 = 0; r0 < kEpiRows; r0 += kRowsPerStore) {
@@ -970,7 +1050,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
             v[x] = __builtin_bit_cast(int, t);
           }
         }
-        const int grow = row0 + half * 64 + r;
+        const int grow = row0 + half * kEpiRows + r;
         const int gcol = col0 + c_lane;
         uint32_t* dst = (uint32_t*)p.C + (size_t)grow * p.N + gcol;
         if (full) {
@@ -1010,6 +1090,30 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       }
     }
   }
+  if constexpr (!PERSIST) {
+    break;
+  } else {
+    if (logical_next >= ntiles) break;
+    // every wave's staging reads are done before the next tile's stage-1
+    // loads refill that space
+    block_barrier();
+    logical = logical_next;
+    logical_next += (int)gridDim.x;
+    tile_of(p, logical, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+    rsrc_a = rsrc_a_next;
+    rsrc_b = rsrc_b_next;
+    set_next();
+    gbase = (gbase + nks) % STAGES;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+  }
+  }   // tiles
 }
 
 // ---------------------------------------------------------------------------
@@ -1725,130 +1829,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   __syncthreads();
   skinny_reduce_store_strided<KIND, MT, NT, WAVES, kPitch, kWaveLds / 4>(p, (const uint32_t*)smem, m0, n0,
                                                                           QA ? row_s : nullptr);
-}
-
-// ---------------------------------------------------------------------------
-// Packed int4 -> FP6 E3M2 operand rows for the E3M2 MFMA.
-//
-// Every int4 value v in [-8, 7] is exact in E3M2 (1 sign, 3 exponent bits
-// with bias 3, 2 mantissa bits): 1 = 1.0 x 2^0, 3 = 1.5 x 2^1, 5 = 1.25 x 2^2,
-// 7 = 1.75 x 2^2, 8 = 1.0 x 2^3, and so on.  A group of 32 values of one row
-// (16 packed bytes) becomes 32 bytes: 32 six-bit codes packed little-endian
-// into 24 bytes, then 8 zero bytes, so a row of K values takes K bytes and
-// a group is two 16-byte chunks (the layout the LDS swizzle works in).
-//
-// Within a group the codes are stored in the order k = 0, 2, 4, 6, 1, 3, 5,
-// 7, 8, 10, ...: even and odd nibbles of each packed dword are looked up
-// separately.  The MFMA pairs slot i of A with slot i of B, and both
-// operands use this order, so the sum over k is unchanged.
-//
-// Code lookup, four nibbles at a time: v_perm_b32 picks bytes from an
-// eight-byte table, one table for nibbles 0..7 (v = 0..7) and one for
-// 8..15 (v = -8..-1); the nibble's bit 3 selects between them.
-__device__ __forceinline__ uint32_t e3m2_codes(uint32_t nib4) {
-  // table bytes: codes of v = 0..7 and of v = -8..-1
-  constexpr uint32_t kPosLo = 0x12100C00u, kPosHi = 0x17161514u;
-  constexpr uint32_t kNegLo = 0x35363738u, kNegHi = 0x2C303234u;
-  const uint32_t idx = nib4 & 0x07070707u;
-  const uint32_t pos = __builtin_amdgcn_perm(kPosHi, kPosLo, idx);
-  const uint32_t neg = __builtin_amdgcn_perm(kNegHi, kNegLo, idx);
-  const uint32_t mask = ((nib4 >> 3) & 0x01010101u) * 0xFFu;   // 0xFF where v < 0
-  return (neg & mask) | (pos & ~mask);
-}
-// four six-bit codes (one per byte) -> 24 contiguous bits
-__device__ __forceinline__ uint32_t pack4_6bit(uint32_t c) {
-  return (c & 0x3Fu) | ((c >> 2) & 0xFC0u) | ((c >> 4) & 0x3F000u) | ((c >> 6) & 0xFC0000u);
-}
-
-__global__ __launch_bounds__(256) void pack_i4_e3m2(const uint8_t* __restrict__ src,
-                                                    uint8_t* __restrict__ dst, int64_t groups) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= groups) return;
-  const i32x4 x = ((const i32x4*)src)[g];
-  uint32_t q[8];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t w = (uint32_t)x[d];
-    q[2 * d] = pack4_6bit(e3m2_codes(w & 0x0F0F0F0Fu));          // k = 8d, 8d+2, 8d+4, 8d+6
-    q[2 * d + 1] = pack4_6bit(e3m2_codes((w >> 4) & 0x0F0F0F0Fu)); // k = 8d+1, ..., 8d+7
-  }
-  // eight 24-bit pieces -> six dwords
-  const i32x4 lo = {(int)(q[0] | (q[1] << 24)), (int)((q[1] >> 8) | (q[2] << 16)),
-                    (int)((q[2] >> 16) | (q[3] << 8)), (int)(q[4] | (q[5] << 24))};
-  const i32x4 hi = {(int)((q[5] >> 8) | (q[6] << 16)), (int)((q[6] >> 16) | (q[7] << 8)), 0, 0};
-  ((i32x4*)dst)[2 * g] = lo;
-  ((i32x4*)dst)[2 * g + 1] = hi;
-}
-
-
-// Rows of at most 512 * WPR * NC halves, held in registers: WPR wavefronts
-// share a row (a workgroup of four waves takes 4 / WPR rows) and each lane
-// keeps its NC 16-byte chunks (chunk li + 64 WPR c, li the lane's index
-// within the row), so the row is read once for both passes.  Chunks past the
-// row end load as zero through the buffer resource, which leaves the absmax
-// unchanged.  WPR = 4 spreads a row over 256 lanes for short M (the rounding
-// pass is ALU latency there); WPR = 1 needs no LDS and no barrier.
-template <int WPR, int NC>
-__global__ __launch_bounds__(256) void quantize_rows_f16_regs(const uint8_t* __restrict__ X,
-                                                              int8_t* __restrict__ Q,
-                                                              float* __restrict__ scale, int M,
-                                                              int K) {
-  static_assert(WPR == 1 || WPR == 4, "a row takes one wave or the whole workgroup");
-  constexpr int kRowLanes = 64 * WPR;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row = blockIdx.x * (4 / WPR) + wave / WPR;
-  const int li = threadIdx.x - (wave / WPR) * kRowLanes;
-  if (WPR == 1 && row >= M) return;   // with WPR = 4 the grid has exactly M workgroups
-  const int chunks = K >> 3;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(X + (size_t)row * K * 2), 0, K * 2, kBufferWord3);
-  i32x4 v[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-    v[c] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)(li + kRowLanes * c) * 16u, 0, 0);
-  float amax = 0.f;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) amax = absmax8(__builtin_bit_cast(f16x8, v[c]), amax);
-  amax = wave_max(amax);
-  if constexpr (WPR > 1) {
-    __shared__ float part[4];
-    if ((threadIdx.x & 63) == 0) part[wave] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-  }
-  const float s = __fdiv_rn(amax, 127.0f);
-  if (li == 0) scale[row] = s;
-  const float r = __fdiv_rn(1.0f, s);
-  uint64_t* qrow = (uint64_t*)(Q + (size_t)row * K);
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int idx = li + kRowLanes * c;
-    if (idx < chunks) qrow[idx] = s != 0.f ? quantize8(__builtin_bit_cast(f16x8, v[c]), s, r) : 0;
-  }
-}
-
-// Longer rows (and K = 0): one workgroup per row and two passes over it, the
-// second re-reading the row (mostly from L2).
-__global__ __launch_bounds__(256) void quantize_rows_f16(const uint8_t* __restrict__ X,
-                                                         int8_t* __restrict__ Q,
-                                                         float* __restrict__ scale, int K) {
-  const int row = blockIdx.x;
-  const int chunks = K / 8;   // 16-byte chunks of 8 halves
-  const i32x4* xrow = (const i32x4*)(X + (size_t)row * K * 2);
-  float amax = 0.f;
-  for (int c = threadIdx.x; c < chunks; c += 256)
-    amax = absmax8(__builtin_bit_cast(f16x8, xrow[c]), amax);
-  amax = wave_max(amax);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-  const float s = __fdiv_rn(amax, 127.0f);
-  if (threadIdx.x == 0) scale[row] = s;
-  const float r = __fdiv_rn(1.0f, s);
-  uint64_t* qrow = (uint64_t*)(Q + (size_t)row * K);
-  for (int c = threadIdx.x; c < chunks; c += 256)
-    qrow[c] = s != 0.f ? quantize8(__builtin_bit_cast(f16x8, xrow[c]), s, r) : 0;
 }
 
 }  // namespace lpgemm

@@ -4,7 +4,9 @@
 // checks once per device that the device is gfx950, picks a tile
 // configuration for the shape, and enqueues one kernel on the caller's
 // stream.  Nothing is allocated and no state is kept between calls apart from
-// the per-device property cache.
+// the per-device property cache (and the configuration an ablation pins).
+// The GEMM launches themselves are in run_*.hip (one translation unit per
+// operand kind, see dispatch.hpp).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -13,24 +15,31 @@
 #include <mutex>
 
 #include "../../include/lpgemm.h"
+#include "aux_kernels.hpp"
+#include "dispatch.hpp"
 #include "f64emu_kernels.hpp"
-#include "gemm_kernels.hpp"
 
 namespace lpgemm {
+
 namespace {
-
 constexpr int kMaxDevices = 64;
-
-struct DeviceInfo {
-  bool probed = false;
-  bool is_gfx950 = false;
-  int cu_count = 0;
-};
-
 std::mutex g_device_mutex;
 DeviceInfo g_devices[kMaxDevices];
 
-// Current device's properties, read once per device.
+// LPGEMM_FORCE_CONFIG=<n> in the environment pins a configuration from the
+// library's load on (ablations from the command line); unset or out of
+// range means automatic selection
+int initial_forced_config() {
+  const char* e = std::getenv("LPGEMM_FORCE_CONFIG");
+  if (!e || !*e) return -1;
+  char* end = nullptr;
+  const long v = std::strtol(e, &end, 10);
+  return (end && *end == 0 && v >= 0 && v < CFG_COUNT) ? (int)v : -1;
+}
+}  // namespace
+
+std::atomic<int> g_forced_config{initial_forced_config()};
+
 lpgemm_status current_device(DeviceInfo& out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LPGEMM_ERROR_ARCH;
@@ -47,394 +56,6 @@ lpgemm_status current_device(DeviceInfo& out) {
   return d.is_gfx950 ? LPGEMM_SUCCESS : LPGEMM_ERROR_ARCH;
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-
-// Host-only argument checks, in the order the header documents.  Sets
-// `nothing_to_do` when the product is empty (M or N is zero).
-lpgemm_status validate(Kind kind, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
-                       const void* C, const void* rs, const void* cs, bool& nothing_to_do) {
-  nothing_to_do = false;
-  if (M < 0 || N < 0 || K < 0) return LPGEMM_ERROR_INVALID_VALUE;
-  if (M > INT32_MAX || N > INT32_MAX) return LPGEMM_ERROR_INVALID_VALUE;
-  switch (kind) {
-    case KIND_I8:
-    case KIND_I8_DEQUANT:
-    case KIND_I8_MOD:
-      if (K % 16 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
-      break;
-    case KIND_I4:
-    case KIND_I4_E3M2:
-      if (K % 32 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
-      break;
-    case KIND_F16:
-      if (K % 8 != 0 || K > LPGEMM_MAX_K_F16) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
-      break;
-  }
-  if (M == 0 || N == 0) {
-    nothing_to_do = true;
-    return LPGEMM_SUCCESS;
-  }
-  if (!C) return LPGEMM_ERROR_INVALID_VALUE;
-  if (K > 0 && (!A || !B)) return LPGEMM_ERROR_INVALID_VALUE;
-  if (kind == KIND_I8_DEQUANT && (!rs || !cs)) return LPGEMM_ERROR_INVALID_VALUE;
-  if (!aligned16(C)) return LPGEMM_ERROR_MISALIGNED;
-  if (K > 0 && (!aligned16(A) || !aligned16(B))) return LPGEMM_ERROR_MISALIGNED;
-  if (kind == KIND_I8_DEQUANT && (!aligned4(rs) || !aligned4(cs))) return LPGEMM_ERROR_MISALIGNED;
-  return LPGEMM_SUCCESS;
-}
-
-// Kernel configurations.  The four-wave direct-to-LDS kernel with 256 x 256
-// tiles has the best operand reuse; smaller tiles fill the 256 CUs when the
-// product has few 256 x 256 tiles.
-enum KernelCfg {
-  CFG_256_S2_R128 = 0,   // 4 waves, 256 x 256, 2 stages of 128-byte rows (see kNtC)
-  CFG_256_S4_R64 = 1,    // 4 waves, 256 x 256, 4 stages of 64-byte rows
-  CFG_256_S3_R64 = 2,    // 4 waves, 256 x 256, 3 stages of 64-byte rows
-  CFG_128_S4_R64 = 3,    // 4 waves, 128 x 128, 4 stages of 64-byte rows
-  CFG_V1_256x256 = 4,    // 8 waves, 128 x 64 per wave, register-staged loads
-  CFG_V1_128x128 = 5,    // 4 waves, 64 x 64 per wave, register-staged loads
-  CFG_V1_64x64 = 6,      // 4 waves, 32 x 32 per wave, register-staged loads
-  CFG_PP_R64 = 7,        // 8 waves ping-pong, 256 x 256, 4 stages of 64-byte rows
-  CFG_SKINNY_32 = 8,     // 32 x 32 tiles, 8 waves split K, 4 K-blocks per load round
-  CFG_SKINNY_64 = 9,     // 64 x 32 tiles, 8 waves split K, 2 K-blocks per load round
-  CFG_SKINNY_32_W16 = 10,  // 32 x 32 tiles, 16 waves split K, 2 K-blocks per load round
-  CFG_SKINNY_LDS_R2 = 11,  // 32 x 32 tiles, 8 waves split K, B through LDS, 2 K-blocks per round
-  CFG_SKINNY_LDS_R4 = 12,  // 32 x 32 tiles, 8 waves split K, B through LDS, 4 K-blocks per round
-  CFG_SKINNY_LDS_W4 = 13,  // 32 x 32 tiles, 4 waves split K, B through LDS, 4 K-blocks per round
-  CFG_SKINNY_PIPE_W4R2 = 14,  // as 13, double-buffered rounds of 2 K-blocks
-  CFG_SKINNY_PIPE_W8R1 = 15,  // 8 waves, double-buffered rounds of 1 K-block
-  CFG_SKINNY_PIPE_W4R3 = 16,  // 4 waves, double-buffered rounds of 3 K-blocks
-  CFG_SKINNY_PIPE_W8R2 = 17,  // 8 waves, double-buffered rounds of 2 K-blocks
-  CFG_128x64_S4_R64 = 18,     // 4 waves, 128 x 64, 4 stages of 64-byte rows
-  CFG_256x128_S4_R64 = 19,    // 4 waves, 256 x 128, 4 stages of 64-byte rows
-  CFG_128x64_S6_R128 = 20,    // 4 waves, 128 x 64, 6 stages of 128-byte rows
-  CFG_128x64_S8_R64 = 21,     // 4 waves, 128 x 64, 8 stages of 64-byte rows
-  CFG_128_S4_R128 = 22,       // 4 waves, 128 x 128, 4 stages of 128-byte rows
-  // ablations of configuration 0
-  CFG_256_S2_R128_NT = 23,       // operand loads non-temporal (nt)
-  CFG_256_S2_R128_SC0 = 24,      // operand loads sc0
-  CFG_256_S2_R128_SC01 = 25,     // operand loads sc0 sc1
-  CFG_256_S2_R128_SPLIT = 26,    // split loader: two waves load A, two load B
-  CFG_256_S2_R128_L1 = 27,       // the next stage's loads all issued in K-step 0
-  CFG_256_S2_R128_LALL = 28,     // ... spread over all K-steps but the last
-  CFG_256_S2_R128_CACHED_C = 29, // C written with ordinary (cached) stores
-  CFG_256_S2_R128_B4 = 30,       // stage barrier after 4 of the last K-step's 16 MFMAs
-  CFG_256_S2_R128_B12 = 31,      // ... after 12
-  CFG_256_S5_R64_NT = 32,        // 4 waves, 256 x 256, 5 stages of 64-byte rows (all 160 KiB), NT C
-  CFG_256_S4_R64_NT = 33,        // 4 waves, 256 x 256, 4 stages of 64-byte rows, NT C
-  CFG_128x64_S3_R256 = 34,       // 4 waves, 128 x 64, 3 stages of 256-byte rows
-  CFG_128_S5_R128 = 35,          // 4 waves, 128 x 128, 5 stages of 128-byte rows (all 160 KiB)
-  CFG_128_S2_R256 = 36,          // 4 waves, 128 x 128, 2 stages of 256-byte rows
-  CFG_256_S2_R128_PF = 37,       // configuration 0 plus an L2 prefetch of the stage after next
-  CFG_256_S2_R128_SCHED = 38,    // configuration 0 with the loads placed by the compiler's schedule
-  CFG_128_S2_R256_PIN = 39,      // configuration 36 with one MFMA pinned in front of each load
-  CFG_128_S4_R128_PIN = 40,      // configuration 22 with one MFMA pinned in front of each load
-  CFG_128x64_S3_R256_PIN = 41,   // configuration 34 with one MFMA pinned in front of each load
-  CFG_256_S2_R128_PIN_L1 = 42,   // configuration 0 with all of a stage's loads pinned in K-step 0
-  CFG_256_S2_R128_PIN_L3 = 43,   // configuration 0 with the loads pinned over K-steps 0-2
-  CFG_256_S2_R128_PIN_I4 = 44,   // configuration 0 with pinned loads also for int4
-  CFG_256_S2_R128_PIN_E3M2 = 45, // E3M2 on configuration 0 with one MFMA pinned in front of each load
-  CFG_256_S2_R128_PIN_KXN = 46,  // K x N B on configuration 0 with one MFMA pinned in front of each load
-  CFG_COUNT = 47
-};
-
-// Row bytes of one LDS K-stage for a configuration (the register-staged
-// kernels expand int4 to int8 on the way into LDS, 128 values per stage).
-int stage_row_bytes(KernelCfg c) {
-  return (c == CFG_256_S4_R64 || c == CFG_256_S3_R64 || c == CFG_128_S4_R64 || c == CFG_PP_R64 ||
-          c == CFG_128x64_S4_R64 || c == CFG_256x128_S4_R64 || c == CFG_128x64_S8_R64 ||
-          c == CFG_256_S5_R64_NT || c == CFG_256_S4_R64_NT)
-             ? 64
-             : ((c == CFG_128x64_S3_R256 || c == CFG_128_S2_R256) ? 256 : 128);
-}
-bool expands_int4_in_lds(KernelCfg c) { return c >= CFG_V1_256x256 && c <= CFG_V1_64x64; }
-bool is_skinny(KernelCfg c) { return c >= CFG_SKINNY_32 && c <= CFG_SKINNY_PIPE_W8R2; }
-
-int tiles(int64_t x, int t) { return (int)((x + t - 1) / t); }
-
-// LPGEMM_FORCE_CONFIG=<n> pins the kernel configuration (one knob at a time
-// for ablations); unset or out of range means automatic selection.  Read on
-// every call so that a test can walk through the configurations.
-int forced_config() {
-  const char* e = std::getenv("LPGEMM_FORCE_CONFIG");
-  if (!e || !*e) return -1;
-  char* end = nullptr;
-  const long v = std::strtol(e, &end, 10);
-  return (end && *end == 0 && v >= 0 && v < CFG_COUNT) ? (int)v : -1;
-}
-
-// The E3M2 kind runs only on the LDS-pipelined kernels with 128-byte stage
-// rows (two 64-value MFMA steps per stage); the reduced int8 kind of the
-// fp64 emulation uses the same three.
-bool supports_e3m2(int c) {
-  return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128 || c == CFG_256_S2_R128_PIN_E3M2;
-}
-
-KernelCfg choose_config_e3m2(int64_t M, int64_t N, int cu_count) {
-  const int f = forced_config();
-  if (f >= 0 && supports_e3m2(f)) return (KernelCfg)f;
-  if (M <= 128) return CFG_128x64_S6_R128;
-  if ((int64_t)tiles(M, 256) * tiles(N, 256) >= cu_count) return CFG_256_S2_R128;
-  if ((int64_t)tiles(M, 128) * tiles(N, 128) >= cu_count / 2) return CFG_128_S4_R128;
-  return CFG_128x64_S6_R128;
-}
-
-KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
-  const int f = forced_config();
-  // configurations 45 and 46 differ from 0 only for the E3M2 kind and for
-  // K x N B
-  if (f == CFG_256_S2_R128_PIN_E3M2 || f == CFG_256_S2_R128_PIN_KXN) return CFG_256_S2_R128;
-  if (f >= 0) return (KernelCfg)f;
-  const bool int8_rows = kind == KIND_I8 || kind == KIND_I8_DEQUANT;
-  // few rows against many columns: stream B with split-K workgroups
-  if (M <= 32) return CFG_SKINNY_PIPE_W4R2;
-  if (M <= 64) return CFG_SKINNY_64;
-  // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128.
-  // int8 rows stream B in 256-byte pieces per stage (M = 128, K = 4096,
-  // N = 14336: 19.2 us against 20.4 us with six 128-byte stages)
-  if (M <= 128) return int8_rows ? CFG_128x64_S3_R256 : CFG_128x64_S6_R128;
-  const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
-  if (big >= cu_count) return CFG_256_S2_R128;
-  // 128 x 128 tiles: at 2048^3, two 256-byte stages for int8 and int4
-  // (14.5 / 15.0 us against 15.4 / 15.7 us with four 64-byte stages), four
-  // 128-byte stages for fp16 (23.1 against 25.4 us)
-  const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
-  if (mid >= cu_count / 2) return kind == KIND_F16 ? CFG_128_S4_R128 : CFG_128_S2_R256;
-  return CFG_V1_64x64;
-}
-
-template <int BM, int BN>
-lpgemm_status launch(const void* fn, GemmArgs args, int threads, hipStream_t stream) {
-  args.tiles_m = tiles(args.M, BM);
-  args.tiles_n = tiles(args.N, BN);
-  args.group_m = 8;
-  const int64_t nblocks = (int64_t)args.tiles_m * args.tiles_n;
-  if (nblocks > INT32_MAX) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
-  void* kargs[] = {&args};
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(threads), kargs, 0, stream);
-  return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
-}
-
-// B stored K x N row-major runs on the LDS-pipelined kernels with 128-byte
-// stage rows: 128 k-rows of B per stage.
-bool supports_kxn(int c) {
-  return c == CFG_256_S2_R128 || c == CFG_128x64_S6_R128 || c == CFG_128_S4_R128 || c == CFG_256_S2_R128_PIN_KXN;
-}
-
-KernelCfg choose_config_kxn(int64_t M, int64_t N, int cu_count) {
-  const int f = forced_config();
-  if (f >= 0 && supports_kxn(f)) return (KernelCfg)f;
-  if (M <= 128) return CFG_128x64_S6_R128;
-  if ((int64_t)tiles(M, 256) * tiles(N, 256) >= cu_count) return CFG_256_S2_R128;
-  if ((int64_t)tiles(M, 128) * tiles(N, 128) >= cu_count / 2) return CFG_128_S4_R128;
-  return CFG_128x64_S6_R128;
-}
-
-template <int KIND, bool BKN = false>
-lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
-                  const float* rs, const float* cs, hipStream_t stream, int modulus = 0) {
-  // K x N B: k-rows of N bytes must start 16-byte aligned and the matrix
-  // must fit the 32-bit offsets of its buffer resource (a shape error, so it
-  // ranks with the K checks: after negative sizes, before pointers)
-  if (BKN && M > 0 && N > 0 && K >= 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX &&
-      (N % 16 != 0 || K * N >= ((int64_t)1 << 31)))
-    return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
-  bool nothing_to_do = false;
-  lpgemm_status st = validate((Kind)KIND, M, N, K, A, B, C, rs, cs, nothing_to_do);
-  if (st != LPGEMM_SUCCESS || nothing_to_do) return st;
-  DeviceInfo dev;
-  st = current_device(dev);
-  if (st != LPGEMM_SUCCESS) return st;
-
-  GemmArgs args{};
-  args.A = static_cast<const uint8_t*>(A);
-  args.B = static_cast<const uint8_t*>(B);
-  args.C = C;
-  args.row_scale = rs;
-  args.col_scale = cs;
-  args.M = (int)M;
-  args.N = (int)N;
-  args.modulus = modulus;
-  args.inv_modulus = modulus > 0 ? 1.0 / (double)modulus : 0.0;
-  // bytes per operand row: fp16 2K, packed int4 K/2, int8 and E3M2 K
-  const int64_t row_bytes = KIND == KIND_F16 ? 2 * K : (KIND == KIND_I4 ? K / 2 : K);
-  args.row_bytes = (int)row_bytes;
-
-  const KernelCfg cfg = BKN ? choose_config_kxn(M, N, dev.cu_count)
-                      : (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) ? choose_config_e3m2(M, N, dev.cu_count)
-                                             : choose_config(M, N, dev.cu_count, KIND);
-  const int64_t stage_bytes = (KIND == KIND_I4 && expands_int4_in_lds(cfg)) ? K : row_bytes;
-  (void)is_skinny;
-  const int rowb = stage_row_bytes(cfg);
-  args.k_stages = (int)((stage_bytes + rowb - 1) / rowb);
-  // Configuration 0 writes C with non-temporal stores, except for int4,
-  // whose shorter main loop measured faster with cached stores (8192^3,
-  // steady state: int8 +2%, fp16 +2%, int4 -1%); the byte stores of the
-  // reduced kind go through the direct path, where the choice does not
-  // apply.  On the general and K x N paths it also issues the next stage's
-  // loads in its first two K-steps (int8 +1.5%, fp16 +2%).
-  constexpr bool kNtC = KIND != KIND_I4 && KIND != KIND_I8_MOD;
-  // ... and pins one MFMA in front of each of a K-step's loads (8192^3, one
-  // MI355X: int8 2306 against 2271 TOP/s, fp16 1221 against 1182 TFLOP/s),
-  // except for int4, whose expanded operands would then spill
-  constexpr bool kPinLoads = KIND != KIND_I4;
-
-  if constexpr (BKN) {
-    switch (cfg) {
-      case CFG_256_S2_R128_PIN_KXN:
-        return launch<256, 256>(
-            (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, true, 2, true, 0, false, true>, args, 256,
-            stream);
-      case CFG_256_S2_R128:
-        return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, true, 2, true>, args,
-                                256, stream);
-      case CFG_128_S4_R128:
-        return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128, 0, false, true>, args, 256,
-                                stream);
-      default:
-        return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128, 0, false, true>, args, 256,
-                               stream);
-    }
-  } else if constexpr (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) {
-    switch (cfg) {
-      case CFG_256_S2_R128_PIN_E3M2:
-        return launch<256, 256>(
-            (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 0, kNtC, 0, false, true>, args, 256,
-            stream);
-      case CFG_256_S2_R128:
-        return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 0, kNtC>, args,
-                                256, stream);
-      case CFG_128_S4_R128:
-        return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
-      default:
-        return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128>, args, 256, stream);
-    }
-  } else {
-  switch (cfg) {
-    case CFG_256_S2_R128:
-      return launch<256, 256>(
-          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads>, args, 256,
-          stream);
-    case CFG_128_S4_R128:
-      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
-    case CFG_256_S4_R64:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 4, 64>, args, 256, stream);
-    case CFG_256_S3_R64:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 3, 64>, args, 256, stream);
-    case CFG_128_S4_R64:
-      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 64>, args, 256, stream);
-    case CFG_V1_256x256:
-      return launch<256, 256>((const void*)&gemm_tiled<KIND, 256, 256, 2, 4>, args, 512, stream);
-    case CFG_V1_128x128:
-      return launch<128, 128>((const void*)&gemm_tiled<KIND, 128, 128, 2, 2>, args, 256, stream);
-    case CFG_PP_R64:
-      return launch<256, 256>((const void*)&gemm_pingpong<KIND, 64>, args, 512, stream);
-    case CFG_SKINNY_32:
-      return launch<32, 32>((const void*)&gemm_skinny<KIND, 1, 8, 4>, args, 512, stream);
-    case CFG_SKINNY_64:
-      return launch<64, 32>((const void*)&gemm_skinny<KIND, 2, 8, 2>, args, 512, stream);
-    case CFG_SKINNY_32_W16:
-      return launch<32, 32>((const void*)&gemm_skinny<KIND, 1, 16, 2>, args, 1024, stream);
-    case CFG_SKINNY_LDS_R2:
-      return launch<32, 32>((const void*)&gemm_skinny_lds<KIND, 8, 2>, args, 512, stream);
-    case CFG_SKINNY_LDS_R4:
-      return launch<32, 32>((const void*)&gemm_skinny_lds<KIND, 8, 4>, args, 512, stream);
-    case CFG_SKINNY_LDS_W4:
-      return launch<32, 32>((const void*)&gemm_skinny_lds<KIND, 4, 4>, args, 256, stream);
-    case CFG_SKINNY_PIPE_W4R2:
-      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 4, 2>, args, 256, stream);
-    case CFG_SKINNY_PIPE_W8R1:
-      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 8, 1>, args, 512, stream);
-    case CFG_SKINNY_PIPE_W4R3:
-      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 4, 3>, args, 256, stream);
-    case CFG_SKINNY_PIPE_W8R2:
-      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 8, 2>, args, 512, stream);
-    case CFG_128x64_S4_R64:
-      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 4, 64>, args, 256, stream);
-    case CFG_256x128_S4_R64:
-      return launch<256, 128>((const void*)&gemm_v3<KIND, 256, 128, 4, 64>, args, 256, stream);
-    case CFG_128x64_S6_R128:
-      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128>, args, 256, stream);
-    case CFG_128x64_S8_R64:
-      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 8, 64>, args, 256, stream);
-    case CFG_128x64_S3_R256:
-      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 3, 256>, args, 256, stream);
-    case CFG_128_S5_R128:
-      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 5, 128>, args, 256, stream);
-    case CFG_128_S2_R256:
-      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 2, 256>, args, 256, stream);
-    case CFG_128_S2_R256_PIN:
-      return launch<128, 128>(
-          (const void*)&gemm_v3<KIND, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, kPinLoads>, args, 256,
-          stream);
-    case CFG_128_S4_R128_PIN:
-      return launch<128, 128>(
-          (const void*)&gemm_v3<KIND, 128, 128, 4, 128, 0, false, false, 0, false, 0, false, kPinLoads>, args, 256,
-          stream);
-    case CFG_128x64_S3_R256_PIN:
-      return launch<128, 64>(
-          (const void*)&gemm_v3<KIND, 128, 64, 3, 256, 0, false, false, 0, false, 0, false, kPinLoads>, args, 256,
-          stream);
-    case CFG_256_S2_R128_PIN_L1:
-      return launch<256, 256>(
-          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 1, kNtC, 0, false, kPinLoads>, args, 256,
-          stream);
-    case CFG_256_S2_R128_PIN_L3:
-      return launch<256, 256>(
-          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 3, kNtC, 0, false, kPinLoads>, args, 256,
-          stream);
-    case CFG_256_S2_R128_PIN_I4:
-      return launch<256, 256>(
-          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, true>, args, 256,
-          stream);
-    case CFG_256_S2_R128_SCHED:
-      return launch<256, 256>(
-          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, false>, args, 256,
-          stream);
-    case CFG_256_S2_R128_PF:
-      return launch<256, 256>(
-          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, true>, args, 256, stream);
-    case CFG_256_S2_R128_NT:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 1>, args, 256, stream);
-    case CFG_256_S2_R128_SC0:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 2>, args, 256, stream);
-    case CFG_256_S2_R128_SC01:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 4>, args, 256, stream);
-    case CFG_256_S2_R128_SPLIT:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, true>, args, 256, stream);
-    case CFG_256_S2_R128_L1:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 1>, args, 256,
-                              stream);
-    case CFG_256_S2_R128_CACHED_C:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, false>, args,
-                              256, stream);
-    case CFG_256_S2_R128_B4:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 4>, args,
-                              256, stream);
-    case CFG_256_S2_R128_B12:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 12>, args,
-                              256, stream);
-    case CFG_256_S5_R64_NT:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 5, 64, 0, false, false, 0, kNtC>, args, 256,
-                              stream);
-    case CFG_256_S4_R64_NT:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 4, 64, 0, false, false, 0, kNtC>, args, 256,
-                              stream);
-    case CFG_256_S2_R128_LALL:
-      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
-    case CFG_V1_64x64:
-      return launch<64, 64>((const void*)&gemm_tiled<KIND, 64, 64, 2, 2>, args, 256, stream);
-    default:
-      // every configuration the choosers can return has a case above; the
-      // stage count was derived from the configuration, so no other kernel
-      // may stand in for one
-      return LPGEMM_ERROR_INVALID_VALUE;
-  }
-  }
-}
-
-}  // namespace
 }  // namespace lpgemm
 
 using namespace lpgemm;
@@ -784,6 +405,13 @@ const char* lpgemm_status_string(lpgemm_status status) {
   return "unknown status";
 }
 
-int lpgemm_version(void) { return 100; }
+int lpgemm_version(void) { return 200; }
+
+int lpgemm_config_count(void) { return CFG_COUNT; }
+
+int lpgemm_force_config(int config) {
+  const int v = (config >= 0 && config < CFG_COUNT) ? config : -1;
+  return g_forced_config.exchange(v);
+}
 
 }  // extern "C"

@@ -1,0 +1,7 @@
+// The int8 with dequantisation GEMM kernels: every configuration of run<KIND_I8_DEQUANT>.
+#include "run_kernels.hpp"
+
+namespace lpgemm {
+template lpgemm_status run<KIND_I8_DEQUANT, false>(int64_t, int64_t, int64_t, const void*, const void*, void*, const float*,
+                                       const float*, hipStream_t, int);
+}  // namespace lpgemm

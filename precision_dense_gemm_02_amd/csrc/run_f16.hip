@@ -1,0 +1,7 @@
+// The fp16 GEMM kernels: every configuration of run<KIND_F16>.
+#include "run_kernels.hpp"
+
+namespace lpgemm {
+template lpgemm_status run<KIND_F16, false>(int64_t, int64_t, int64_t, const void*, const void*, void*, const float*,
+                                       const float*, hipStream_t, int);
+}  // namespace lpgemm

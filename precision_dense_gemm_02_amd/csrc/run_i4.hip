@@ -1,0 +1,7 @@
+// The packed int4 GEMM kernels: every configuration of run<KIND_I4>.
+#include "run_kernels.hpp"
+
+namespace lpgemm {
+template lpgemm_status run<KIND_I4, false>(int64_t, int64_t, int64_t, const void*, const void*, void*, const float*,
+                                       const float*, hipStream_t, int);
+}  // namespace lpgemm

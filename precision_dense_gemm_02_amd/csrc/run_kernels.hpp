@@ -1,0 +1,223 @@
+// Definition of run<KIND, BKN>: the kernel launch for each configuration.
+// Included only by the run_*.hip translation units, each of which
+// instantiates it for one operand kind.
+#pragma once
+
+#include "dispatch.hpp"
+
+namespace lpgemm {
+
+template <int KIND, bool BKN>
+lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
+                  const float* rs, const float* cs, hipStream_t stream, int modulus) {
+  // K x N B: k-rows of N bytes must start 16-byte aligned and the matrix
+  // must fit the 32-bit offsets of its buffer resource (a shape error, so it
+  // ranks with the K checks: after negative sizes, before pointers)
+  if (BKN && M > 0 && N > 0 && K >= 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX &&
+      (N % 16 != 0 || K * N >= ((int64_t)1 << 31)))
+    return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  bool nothing_to_do = false;
+  lpgemm_status st = validate((Kind)KIND, M, N, K, A, B, C, rs, cs, nothing_to_do);
+  if (st != LPGEMM_SUCCESS || nothing_to_do) return st;
+  DeviceInfo dev;
+  st = current_device(dev);
+  if (st != LPGEMM_SUCCESS) return st;
+
+  GemmArgs args{};
+  args.A = static_cast<const uint8_t*>(A);
+  args.B = static_cast<const uint8_t*>(B);
+  args.C = C;
+  args.row_scale = rs;
+  args.col_scale = cs;
+  args.M = (int)M;
+  args.N = (int)N;
+  args.modulus = modulus;
+  args.inv_modulus = modulus > 0 ? 1.0 / (double)modulus : 0.0;
+  // bytes per operand row: fp16 2K, packed int4 K/2, int8 and E3M2 K
+  const int64_t row_bytes = KIND == KIND_F16 ? 2 * K : (KIND == KIND_I4 ? K / 2 : K);
+  args.row_bytes = (int)row_bytes;
+
+  const KernelCfg cfg = BKN ? choose_config_kxn(M, N, dev.cu_count)
+                      : (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) ? choose_config_e3m2(M, N, dev.cu_count)
+                                             : choose_config(M, N, dev.cu_count, KIND);
+  const int64_t stage_bytes = (KIND == KIND_I4 && expands_int4_in_lds(cfg)) ? K : row_bytes;
+  const int rowb = stage_row_bytes(cfg);
+  args.k_stages = (int)((stage_bytes + rowb - 1) / rowb);
+  // Configuration 0 writes C with non-temporal stores, except for int4,
+  // whose shorter main loop measured faster with cached stores (8192^3,
+  // steady state: int8 +2%, fp16 +2%, int4 -1%); the byte stores of the
+  // reduced kind go through the direct path, where the choice does not
+  // apply.  On the general and K x N paths it also issues the next stage's
+  // loads in its first two K-steps (int8 +1.5%, fp16 +2%).
+  constexpr bool kNtC = KIND != KIND_I4 && KIND != KIND_I8_MOD;
+  // ... and pins one MFMA in front of each of a K-step's loads (8192^3, one
+  // MI355X: int8 2306 against 2271 TOP/s, fp16 1221 against 1182 TFLOP/s),
+  // except for int4, whose expanded operands would then spill
+  constexpr bool kPinLoads = KIND != KIND_I4;
+
+  if constexpr (BKN) {
+    switch (cfg) {
+      case CFG_256_S2_R128_PIN_KXN:
+        return launch<256, 256>(
+            (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, true, 2, true, 0, false, true>, args, 256,
+            stream);
+      case CFG_256_S2_R128:
+        return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, true, 2, true>, args,
+                                256, stream);
+      case CFG_128_S4_R128:
+        return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128, 0, false, true>, args, 256,
+                                stream);
+      default:
+        return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128, 0, false, true>, args, 256,
+                               stream);
+    }
+  } else if constexpr (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) {
+    switch (cfg) {
+      case CFG_256_S2_R128_PIN_E3M2:
+        return launch<256, 256>(
+            (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 0, kNtC, 0, false, true>, args, 256,
+            stream);
+      case CFG_256_S2_R128:
+        return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 0, kNtC>, args,
+                                256, stream);
+      case CFG_128_S4_R128:
+        return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
+      default:
+        return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128>, args, 256, stream);
+    }
+  } else {
+  switch (cfg) {
+    case CFG_256_S2_R128:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_128_S4_R128:
+      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
+    case CFG_256_S2_R128_PERSIST:
+      // int4 keeps configuration 0: its kernel already holds 256 VGPRs, and
+      // the persistent variant's extra state would spill
+      if constexpr (KIND == KIND_I4)
+        return launch<256, 256>(
+            (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads>, args, 256,
+            stream);
+      else
+        return launch_persistent<256, 256>(
+            (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads, true>,
+            args, 256, stream, dev.cu_count);
+    case CFG_256_S4_R64:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 4, 64>, args, 256, stream);
+    case CFG_256_S3_R64:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 3, 64>, args, 256, stream);
+    case CFG_128_S4_R64:
+      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 64>, args, 256, stream);
+    case CFG_V1_256x256:
+      return launch<256, 256>((const void*)&gemm_tiled<KIND, 256, 256, 2, 4>, args, 512, stream);
+    case CFG_V1_128x128:
+      return launch<128, 128>((const void*)&gemm_tiled<KIND, 128, 128, 2, 2>, args, 256, stream);
+    case CFG_PP_R64:
+      return launch<256, 256>((const void*)&gemm_pingpong<KIND, 64>, args, 512, stream);
+    case CFG_SKINNY_32:
+      return launch<32, 32>((const void*)&gemm_skinny<KIND, 1, 8, 4>, args, 512, stream);
+    case CFG_SKINNY_64:
+      return launch<64, 32>((const void*)&gemm_skinny<KIND, 2, 8, 2>, args, 512, stream);
+    case CFG_SKINNY_32_W16:
+      return launch<32, 32>((const void*)&gemm_skinny<KIND, 1, 16, 2>, args, 1024, stream);
+    case CFG_SKINNY_LDS_R2:
+      return launch<32, 32>((const void*)&gemm_skinny_lds<KIND, 8, 2>, args, 512, stream);
+    case CFG_SKINNY_LDS_R4:
+      return launch<32, 32>((const void*)&gemm_skinny_lds<KIND, 8, 4>, args, 512, stream);
+    case CFG_SKINNY_LDS_W4:
+      return launch<32, 32>((const void*)&gemm_skinny_lds<KIND, 4, 4>, args, 256, stream);
+    case CFG_SKINNY_PIPE_W4R2:
+      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 4, 2>, args, 256, stream);
+    case CFG_SKINNY_PIPE_W8R1:
+      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 8, 1>, args, 512, stream);
+    case CFG_SKINNY_PIPE_W4R3:
+      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 4, 3>, args, 256, stream);
+    case CFG_SKINNY_PIPE_W8R2:
+      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 8, 2>, args, 512, stream);
+    case CFG_128x64_S4_R64:
+      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 4, 64>, args, 256, stream);
+    case CFG_256x128_S4_R64:
+      return launch<256, 128>((const void*)&gemm_v3<KIND, 256, 128, 4, 64>, args, 256, stream);
+    case CFG_128x64_S6_R128:
+      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 6, 128>, args, 256, stream);
+    case CFG_128x64_S8_R64:
+      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 8, 64>, args, 256, stream);
+    case CFG_128x64_S3_R256:
+      return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 3, 256>, args, 256, stream);
+    case CFG_128_S5_R128:
+      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 5, 128>, args, 256, stream);
+    case CFG_128_S2_R256:
+      return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 2, 256>, args, 256, stream);
+    case CFG_128_S2_R256_PIN:
+      return launch<128, 128>(
+          (const void*)&gemm_v3<KIND, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_128_S4_R128_PIN:
+      return launch<128, 128>(
+          (const void*)&gemm_v3<KIND, 128, 128, 4, 128, 0, false, false, 0, false, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_128x64_S3_R256_PIN:
+      return launch<128, 64>(
+          (const void*)&gemm_v3<KIND, 128, 64, 3, 256, 0, false, false, 0, false, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_256_S2_R128_PIN_L1:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 1, kNtC, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_256_S2_R128_PIN_L3:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 3, kNtC, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_256_S2_R128_PIN_I4:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, true>, args, 256,
+          stream);
+    case CFG_256_S2_R128_SCHED:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, false>, args, 256,
+          stream);
+    case CFG_256_S2_R128_PF:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, true>, args, 256, stream);
+    case CFG_256_S2_R128_NT:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 1>, args, 256, stream);
+    case CFG_256_S2_R128_SC0:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 2>, args, 256, stream);
+    case CFG_256_S2_R128_SC01:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 4>, args, 256, stream);
+    case CFG_256_S2_R128_SPLIT:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, true>, args, 256, stream);
+    case CFG_256_S2_R128_L1:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 1>, args, 256,
+                              stream);
+    case CFG_256_S2_R128_CACHED_C:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, false>, args,
+                              256, stream);
+    case CFG_256_S2_R128_B4:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 4>, args,
+                              256, stream);
+    case CFG_256_S2_R128_B12:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 12>, args,
+                              256, stream);
+    case CFG_256_S5_R64_NT:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 5, 64, 0, false, false, 0, kNtC>, args, 256,
+                              stream);
+    case CFG_256_S4_R64_NT:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 4, 64, 0, false, false, 0, kNtC>, args, 256,
+                              stream);
+    case CFG_256_S2_R128_LALL:
+      return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 2, 128>, args, 256, stream);
+    case CFG_V1_64x64:
+      return launch<64, 64>((const void*)&gemm_tiled<KIND, 64, 64, 2, 2>, args, 256, stream);
+    default:
+      // every configuration the choosers can return has a case above; the
+      // stage count was derived from the configuration, so no other kernel
+      // may stand in for one
+      return LPGEMM_ERROR_INVALID_VALUE;
+  }
+  }
+}
+
+}  // namespace lpgemm

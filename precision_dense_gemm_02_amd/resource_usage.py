@@ -3,8 +3,8 @@ compiler reports them for gfx950.
 
     python -m precision_dense_gemm_02_amd.resource_usage [--all]
 
-Compiles csrc/lpgemm.hip once more with the compiler's resource-usage remarks
-and prints a markdown table.  Without --all only the kernels the automatic
+Compiles every translation unit of csrc/ once more (device code only) with
+the compiler's resource-usage remarks and prints a markdown table.  Without --all only the kernels the automatic
 configuration choice launches are listed.
 """
 from __future__ import annotations
@@ -14,18 +14,22 @@ import re
 import subprocess
 import sys
 
-from .build import CSRC, FLAGS, HIPCC
+from concurrent.futures import ThreadPoolExecutor
+
+from .build import FLAGS, HIPCC, _jobs, sources
 
 # kernels launched by the automatic choice (the name's prefix up to the
 # closing template bracket), and the workloads that run them
 DEFAULT_KERNELS = {
-    "lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true>": "int8, >= 256 tiles of 256x256 (8192^3, 4096^3)",
-    "lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false>": "int4, same shapes",
-    "lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true>": "fp16, same shapes",
-    "lpgemm::gemm_v3<3, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true>": "dequant int8 (LLM M = 2048)",
-    "lpgemm::gemm_v3<0, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false>": "int8, 128x128 tiles (2048^3)",
-    "lpgemm::gemm_v3<2, 128, 128, 4, 128, 0, false, false, 0, false, 0, false, false>": "fp16, 128x128 tiles (2048^3)",
-    "lpgemm::gemm_v3<3, 128, 64, 3, 256, 0, false, false, 0, false, 0, false, false>": "dequant int8, M <= 128 (LLM M = 128)",
+    "lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true>": "int8, >= 2 rounds of 256x256 tiles (8192^3), persistent",
+    "lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false>": "int8, 1-2 rounds of 256x256 tiles (4096^3)",
+    "lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false, false>": "int4, >= 1 round of 256x256 tiles",
+    "lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true>": "fp16, >= 2 rounds (8192^3), persistent",
+    "lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false>": "fp16, 1-2 rounds (4096^3)",
+    "lpgemm::gemm_v3<3, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false>": "dequant int8 (LLM M = 2048)",
+    "lpgemm::gemm_v3<0, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false>": "int8, 128x128 tiles (2048^3)",
+    "lpgemm::gemm_v3<2, 128, 128, 4, 128, 0, false, false, 0, false, 0, false, false, false>": "fp16, 128x128 tiles (2048^3)",
+    "lpgemm::gemm_v3<3, 128, 64, 3, 256, 0, false, false, 0, false, 0, false, false, false>": "dequant int8, M <= 128 (LLM M = 128)",
     "lpgemm::gemm_skinny_pipe<3, 4, 2, false>": "dequant int8, M <= 32 (LLM M = 16)",
     "lpgemm::gemm_tiled<0, 64, 64, 2, 2>": "int8, small grids (1024^3, 512^3)",
     "lpgemm::quantize_rows_f16_regs<4, 2>": "W8A8 row quantiser, short M",
@@ -35,15 +39,20 @@ FIELDS = ["VGPRs", "AGPRs", "TotalSGPRs", "ScratchSize [bytes/lane]", "LDS Size 
           "Occupancy [waves/SIMD]", "VGPRs Spill"]
 
 
-def collect() -> dict:
-    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared",)], "-c", "-o", os.devnull,
-           "-Rpass-analysis=kernel-resource-usage", "--offload-device-only",
-           os.path.join(CSRC, "lpgemm.hip")]
+def _remarks(src: str) -> str:
+    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "-c", "-o", os.devnull,
+           "-Rpass-analysis=kernel-resource-usage", "--offload-device-only", src]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(r.stderr[-2000:])
+    return r.stderr
+
+
+def collect() -> dict:
+    with ThreadPoolExecutor(max_workers=_jobs()) as ex:
+        text = "\n".join(ex.map(_remarks, sources()))
     kernels, cur = {}, None
-    for line in r.stderr.splitlines():
+    for line in text.splitlines():
         m = re.search(r"remark: Function Name: (\S+)", line)
         if m:
             cur = m.group(1)

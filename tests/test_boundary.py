@@ -24,13 +24,28 @@ def test_exports_every_declared_symbol(lib):
                           "lpgemm_i4_e3m2",
                           "lpgemm_i8_kxn", "lpgemm_f64_emu", "lpgemm_f64_emu_moduli",
                           "lpgemm_f64_emu_workspace",
-                          "lpgemm_status_string", "lpgemm_version"}
+                          "lpgemm_status_string", "lpgemm_version", "lpgemm_config_count",
+                          "lpgemm_force_config"}
     for n in names:
         assert hasattr(lib, n), n
 
 
+def test_config_count_and_force_hook(lib):
+    import re
+    src = open(b.HEADER_PATH.replace("include/lpgemm.h",
+                                     "precision_dense_gemm_02_amd/csrc/dispatch.hpp")).read()
+    assert b.config_count() == int(re.search(r"CFG_COUNT = (\d+)", src).group(1))
+    prev = b.force_config(3)
+    try:
+        assert b.force_config(5) == 3
+        assert b.force_config(b.config_count()) == 5      # out of range: automatic
+        assert b.force_config(-7) == -1
+    finally:
+        b.force_config(prev)
+
+
 def test_version_and_strings(lib):
-    assert b.version() == 100
+    assert b.version() == 200
     for code in range(6):
         assert b.status_string(code)
     assert b.status_string(99) == "unknown status"

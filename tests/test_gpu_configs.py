@@ -1,4 +1,4 @@
-"""Every kernel configuration, forced with LPGEMM_FORCE_CONFIG, against the
+"""Every kernel configuration, pinned with lpgemm_force_config, against the
 oracle on ragged shapes (M, N off the tile grid, K with a partial stage)."""
 import os
 
@@ -13,7 +13,16 @@ from precision_dense_gemm_02_amd import inputs  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = range(47)
+def _config_count() -> int:
+    # read from the source so that collection needs no library (the CPU
+    # boundary test checks that the built library reports the same count)
+    import re
+    src = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "precision_dense_gemm_02_amd", "csrc", "dispatch.hpp")
+    return int(re.search(r"CFG_COUNT = (\d+)", open(src).read()).group(1))
+
+
+CONFIGS = range(_config_count())
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -25,9 +34,9 @@ def _gpu():
 
 @pytest.fixture
 def forced(request):
-    os.environ["LPGEMM_FORCE_CONFIG"] = str(request.param)
+    prev = lp.force_config(request.param)
     yield request.param
-    del os.environ["LPGEMM_FORCE_CONFIG"]
+    lp.force_config(prev)
 
 
 def _dev(x):
@@ -113,3 +122,71 @@ def test_skinny_long_k(forced, M):
         torch.cuda.synchronize()
         ref, den = oracle.gemm_f16(f.a, f.b_t)
         assert oracle.f16_rel_error(out.cpu().numpy(), ref, den)["max_rel"] <= 1e-3
+
+
+# the persistent configuration walks several tiles per workgroup: shapes
+# with more 256 x 256 tiles than a 256-CU device has workgroups, ragged
+# edges, and stage counts of both parities (the LDS stage holding a tile's
+# first K-stage then alternates from tile to tile)
+PERSIST_CFG = 47
+
+
+@pytest.mark.parametrize("M,N,K", [(4100, 4100, 16), (4100, 4100, 272), (4100, 4100, 400),
+                                   (8192, 4160, 1040), (8192, 8192, 128)])
+def test_persistent_i8_rounds(M, N, K):
+    print("[case] persistent i8", M, N, K, flush=True)
+    p = inputs.int8_problem(M, N, K, seed=M + N + K)
+    prev = lp.force_config(PERSIST_CFG)
+    try:
+        out = lp.gemm_i8(_dev(p.a), _dev(p.b_t), out=torch.full((M, N), -7, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+    finally:
+        lp.force_config(prev)
+    rows = sorted({r for r in list(range(0, M, 97)) + [M - 1, 255, 256, 4095, 4096] if r < M})
+    np.testing.assert_array_equal(out.cpu().numpy()[rows], oracle.gemm_i8(p.a, p.b_t, rows=rows))
+
+
+@pytest.mark.parametrize("K", [32, 544, 800])
+def test_persistent_i4_rounds(K):
+    M, N = 4100, 4100
+    print("[case] persistent i4", M, N, K, flush=True)
+    p = inputs.int4_problem(M, N, K, seed=K)
+    prev = lp.force_config(PERSIST_CFG)
+    try:
+        out = lp.gemm_i4(_dev(p.a_packed), _dev(p.b_packed), K)
+        torch.cuda.synchronize()
+    finally:
+        lp.force_config(prev)
+    rows = list(range(0, M, 131)) + [M - 1]
+    np.testing.assert_array_equal(out.cpu().numpy()[rows], oracle.gemm_i4(p.a_packed, p.b_packed, K, rows=rows))
+
+
+@pytest.mark.parametrize("K", [8, 136, 200])
+def test_persistent_f16_rounds(K):
+    M, N = 4100, 4100
+    print("[case] persistent f16", M, N, K, flush=True)
+    p = inputs.f16_integer_problem(M, N, K, seed=K)
+    prev = lp.force_config(PERSIST_CFG)
+    try:
+        out = lp.gemm_f16(_dev(p.a), _dev(p.b_t))
+        torch.cuda.synchronize()
+    finally:
+        lp.force_config(prev)
+    rows = list(range(0, M, 131)) + [M - 1]
+    ref = oracle.gemm_i8(p.a.astype(np.int8), p.b_t.astype(np.int8), rows=rows)
+    np.testing.assert_array_equal(out.cpu().numpy()[rows], ref.astype(np.float32))
+
+
+def test_persistent_dequant_llm_2048():
+    # the LLM projection at M = 2048: 448 tiles, a full round and a partial one
+    print("[case] persistent dequant llm 2048", flush=True)
+    p = inputs.llm_problem(2048)
+    prev = lp.force_config(PERSIST_CFG)
+    try:
+        out = lp.gemm_i8_dequant(_dev(p.a), _dev(p.b_t), _dev(p.row_scale), _dev(p.col_scale))
+        torch.cuda.synchronize()
+    finally:
+        lp.force_config(prev)
+    rows = list(range(0, 2048, 61)) + [2047]
+    ref = oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale, rows=rows)
+    np.testing.assert_array_equal(out.cpu().numpy()[rows].view(np.uint32), ref.view(np.uint32))

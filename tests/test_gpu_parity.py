@@ -159,6 +159,59 @@ def test_f16_integer_valued_exact(M, N, K):
     np.testing.assert_array_equal(out.cpu().numpy(), ref.astype(np.float32))
 
 
+class _forced:
+    """Pin one kernel configuration for the duration of a block."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+
+    def __enter__(self):
+        self.prev = lp.force_config(self.cfg)
+
+    def __exit__(self, *exc):
+        lp.force_config(self.prev)
+
+
+def _f16_integer_exact(M, N, K, rows=None, cfg=None):
+    # values in [-8, 7]: |partial sums| <= 64 K < 2^24 for K <= 262143, so
+    # the fp32 sums are exact whatever their order, and must equal the int8
+    # oracle element for element
+    p = inputs.f16_integer_problem(M, N, K, seed=M + 3 * N + 7 * K)
+    a, b = _dev(p.a), _dev(p.b_t)
+    out = _poison_f32(M, N)
+    if cfg is None:
+        lp.gemm_f16(a, b, out=out)
+    else:
+        with _forced(cfg):
+            lp.gemm_f16(a, b, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy() if rows is None else out.cpu().numpy()[rows]
+    ref = oracle.gemm_i8(p.a.astype(np.int8), p.b_t.astype(np.int8), rows=rows)
+    np.testing.assert_array_equal(got, ref.astype(np.float32))
+
+
+def test_f16_integer_valued_exact_benchmarked_8192():
+    # the benchmark's shape and automatic configuration (256 x 256 tiles,
+    # configuration 0, on a 256-CU MI355X): a dropped or repeated k term at
+    # K = 8192 moves an element by an integer, which the 1e-3 bound on N(0,1)
+    # inputs could not see
+    n = 8192
+    _say("f16 integer-valued, benchmarked shape", n)
+    _f16_integer_exact(n, n, n, rows=_sample_rows(n, n=24, seed=11))
+
+
+@pytest.mark.parametrize("cfg,M,N,K", [
+    (0, 4096, 4096, 8192),    # the 256 x 256 kernel timed at 4096^3 and 8192^3
+    (0, 1000, 700, 4112),     # ... on a ragged shape with a partial last stage
+    (22, 2048, 2048, 2048),   # the 128 x 128 fp16 kernel chosen at 2048^3
+    (22, 700, 1100, 1032),
+])
+def test_f16_integer_valued_exact_forced(cfg, M, N, K):
+    _say("f16 integer-valued, configuration", cfg, M, N, K)
+    rows = _sample_rows(M, n=32, seed=cfg + M) if M * N * K > 2 ** 33 else None
+    _f16_integer_exact(M, N, K, rows=rows, cfg=cfg)
+
+
 # ---------------------------------------------------------------- LLM projection
 
 @pytest.mark.parametrize("M", [16, 128])
@@ -268,17 +321,21 @@ def test_int4_range_limit():
 
 # ---------------------------------------------------------------- consistency
 
-def test_cross_path_int4_int8_f16():
-    # the same small integers through the three paths give one answer
-    M, N, K = 700, 530, 1024
+@pytest.mark.parametrize("M,N,K", [(700, 530, 1024), (4096, 4096, 2048)])
+def test_cross_path_int4_int8_f16(M, N, K):
+    # the same small integers through the three paths give one answer; at
+    # 4096 x 4096 all three run the 256 x 256 kernels the benchmark times
     _say("cross path", M, N, K)
-    p = inputs.int4_problem(M, N, K, seed=99)
+    p = inputs.int4_problem(M, N, K, seed=99 + M)
     c4 = lp.gemm_i4(_dev(p.a_packed), _dev(p.b_packed), K)
     c8 = lp.gemm_i8(_dev(p.a_values), _dev(p.b_values))
     cf = lp.gemm_f16(_dev(p.a_values.astype(np.float16)), _dev(p.b_values.astype(np.float16)))
     torch.cuda.synchronize()
     assert torch.equal(c4, c8)
     assert torch.equal(cf, c8.float())
+    rows = _sample_rows(M, n=16, seed=M)
+    np.testing.assert_array_equal(c8.cpu().numpy()[rows],
+                                  oracle.gemm_i8(p.a_values, p.b_values, rows=rows))
 
 
 @pytest.mark.parametrize("kind", ["i8", "f16", "i4"])

@@ -116,6 +116,29 @@ lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double *A, c
                              double *C, int bits, void *workspace, int64_t workspace_bytes,
                              hipStream_t stream);
 
+/* Largest workspace of lpgemm_f64_emu_noalloc: 64 MiB (M = N = K = 1024 at
+ * 53 bits needs about 48 MiB). */
+#define LPGEMM_F64_EMU_NOALLOC_MAX_WORKSPACE (64 * 1024 * 1024)
+
+/* lpgemm_f64_emu for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operation, arguments and result (bit for bit) as lpgemm_f64_emu, but
+ * the intermediates live in a scratch array of
+ * LPGEMM_F64_EMU_NOALLOC_MAX_WORKSPACE bytes that the library holds in the
+ * device memory of each GPU it runs on, from the library's first use on that
+ * GPU until the process ends; the call itself allocates nothing.  Shapes
+ * whose workspace (lpgemm_f64_emu_workspace) exceeds that size return
+ * LPGEMM_ERROR_UNSUPPORTED_SHAPE before anything is enqueued.  Every call on
+ * one GPU shares its scratch, which keeps the last call's contents: calls
+ * that overlap in time on one GPU (on different streams, or from several
+ * host threads) race and give wrong results, so serialise them (for
+ * instance on one stream).  Nothing needs clearing between calls: each call
+ * writes every scratch byte it reads.  Errors as for lpgemm_f64_emu (without
+ * the workspace cases), plus LPGEMM_ERROR_LAUNCH if the scratch's device
+ * address cannot be obtained. */
+lpgemm_status lpgemm_f64_emu_noalloc(int64_t M, int64_t N, int64_t K, const double *A, const double *B,
+                                     double *C, int bits, hipStream_t stream);
+
 /* INT8 with B stored K x N row-major (N contiguous; the "transposed" B of
  * the PTX-vs-WMMA summary page's layout ablation): C = A . B exactly in
  * int32, as lpgemm_i8.  A: M x K int8, B_kxn: K x N int8, C: M x N int32.

@@ -69,6 +69,8 @@ def load_library():
         lib.lpgemm_f64_emu_workspace.restype = _i64
         lib.lpgemm_f64_emu.argtypes = [_i64, _i64, _i64, _p, _p, _p, ctypes.c_int, _p, _i64, _p]
         lib.lpgemm_f64_emu.restype = ctypes.c_int
+        lib.lpgemm_f64_emu_noalloc.argtypes = [_i64, _i64, _i64, _p, _p, _p, ctypes.c_int, _p]
+        lib.lpgemm_f64_emu_noalloc.restype = ctypes.c_int
         lib.lpgemm_i8_kxn.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p]
         lib.lpgemm_i8_kxn.restype = ctypes.c_int
         lib.lpgemm_i4_to_e3m2.argtypes = [_i64, _i64, _p, _p, _p]
@@ -386,4 +388,24 @@ def gemm_f64_emu(a, b_t, bits: int = 53, workspace=None, out=None):
         _check(load_library().lpgemm_f64_emu(M, N, K, a.data_ptr(), b_t.data_ptr(), out.data_ptr(), bits,
                                              workspace.data_ptr(), workspace.numel(),
                                              _stream_handle(dev)), "lpgemm_f64_emu")
+    return out
+
+
+def gemm_f64_emu_noalloc(a, b_t, bits: int = 53, out=None):
+    """gemm_f64_emu without a workspace: the library's own fixed scratch
+    (LPGEMM_F64_EMU_NOALLOC_MAX_WORKSPACE bytes per GPU) holds the
+    intermediates, so the call allocates nothing on the device beyond `out`
+    when it is omitted.  Calls that overlap on one GPU race on that scratch."""
+    torch = _torch()
+    _operand(a, torch.float64, "a")
+    _operand(b_t, torch.float64, "b_t")
+    if a.shape[1] != b_t.shape[1]:
+        raise ValueError(f"K mismatch: a {tuple(a.shape)}, b_t {tuple(b_t.shape)}")
+    dev = _same_device(a, b_t)
+    M, K = a.shape
+    N = b_t.shape[0]
+    out = _output(out, (M, N), torch.float64, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_f64_emu_noalloc(M, N, K, a.data_ptr(), b_t.data_ptr(), out.data_ptr(),
+                                                     bits, _stream_handle(dev)), "lpgemm_f64_emu_noalloc")
     return out

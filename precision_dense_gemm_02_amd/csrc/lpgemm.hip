@@ -60,6 +60,35 @@ lpgemm_status current_device(DeviceInfo& out) {
 
 using namespace lpgemm;
 
+// Device memory of lpgemm_f64_emu_noalloc: the emulation's intermediates
+// (row exponents, residues, reduced products) for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy until the
+// process ends; host code uses only the address hipGetSymbolAddress returns
+// for the current device, never this name.
+static __device__ __align__(256) uint8_t scratch[LPGEMM_F64_EMU_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+
+// The scratch's device address, looked up once per device with that device
+// current (each device has its own copy at its own address).
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64] = {};
+
+lpgemm_status scratch_address(void*& out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return LPGEMM_ERROR_ARCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return LPGEMM_ERROR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  out = g_scratch_ptr[dev];
+  return LPGEMM_SUCCESS;
+}
+
+}  // namespace
+
 namespace {
 
 // fp64 emulation: the moduli, largest first (pairwise coprime)
@@ -188,53 +217,28 @@ unsigned grid_for(int64_t n) {
   return (unsigned)(b < 1 ? 1 : (b > 65536 ? 65536 : b));
 }
 
-}  // namespace
-
-extern "C" {
-
-lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A, const int8_t* B,
-                        int32_t* C, hipStream_t stream) {
-  return run<KIND_I8>(M, N, K, A, B, C, nullptr, nullptr, stream);
-}
-
-lpgemm_status lpgemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t* A_packed,
-                        const uint8_t* B_packed, int32_t* C, hipStream_t stream) {
-  return run<KIND_I4>(M, N, K, A_packed, B_packed, C, nullptr, nullptr, stream);
-}
-
-int lpgemm_f64_emu_moduli(int64_t K, int bits) {
-  if (K < 0 || bits < 1 || bits > 53) return -1;
-  return f64emu_moduli(K, bits);
-}
-
-int64_t lpgemm_f64_emu_workspace(int64_t M, int64_t N, int64_t K, int bits) {
-  if (M < 0 || N < 0 || K < 0 || bits < 1 || bits > 53) return -1;
-  const int s = f64emu_moduli(K, bits);
-  if (s < 0) return -1;
-  return f64emu_layout(M, N, K, s).total;
-}
-
-lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double* A, const double* B,
-                             double* C, int bits, void* workspace, int64_t workspace_bytes,
-                             hipStream_t stream) {
+// Host checks of the fp64 emulation, in the header's order, short of the
+// workspace; sets the modulus count and the workspace layout.  M = 0 or
+// N = 0 returns success with nothing else checked.
+lpgemm_status f64emu_check(int64_t M, int64_t N, int64_t K, const double* A, const double* B, const double* C,
+                           int bits, int& s, F64EmuLayout& L) {
   if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX) return LPGEMM_ERROR_INVALID_VALUE;
   if (bits < 1 || bits > 53) return LPGEMM_ERROR_INVALID_VALUE;
   if (K % 16 != 0 || K > LPGEMM_MAX_K_INT) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
   if (M == 0 || N == 0) return LPGEMM_SUCCESS;
-  if (!C || !workspace) return LPGEMM_ERROR_INVALID_VALUE;
+  if (!C) return LPGEMM_ERROR_INVALID_VALUE;
   if (K > 0 && (!A || !B)) return LPGEMM_ERROR_INVALID_VALUE;
-  const int s = f64emu_moduli(K, bits);
+  s = f64emu_moduli(K, bits);
   if (s < 0) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
-  const F64EmuLayout L = f64emu_layout(M, N, K, s);
-  if (workspace_bytes < L.total) return LPGEMM_ERROR_INVALID_VALUE;
-  if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))) ||
-      ((uintptr_t)workspace & 255) != 0)
-    return LPGEMM_ERROR_MISALIGNED;
-  DeviceInfo dev;
-  lpgemm_status st = current_device(dev);
-  if (st != LPGEMM_SUCCESS) return st;
+  L = f64emu_layout(M, N, K, s);
+  if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B)))) return LPGEMM_ERROR_MISALIGNED;
+  return LPGEMM_SUCCESS;
+}
 
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+// The emulation's launches on `stream`, with its intermediates in `ws`
+// (laid out as L; every byte a launch reads was written by an earlier one).
+lpgemm_status f64emu_enqueue(int64_t M, int64_t N, int64_t K, const double* A, const double* B, double* C,
+                             int bits, int s, const F64EmuLayout& L, uint8_t* ws, hipStream_t stream) {
   int* eA = reinterpret_cast<int*>(ws + L.ea);
   int* eB = reinterpret_cast<int*>(ws + L.eb);
   int8_t* RA = reinterpret_cast<int8_t*>(ws + L.ra);
@@ -267,8 +271,8 @@ lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double* A, c
   // one exact int8 GEMM per modulus, its epilogue reducing modulo m
   const int64_t cr_stride = align256(M * N);   // bytes between products
   for (int l = 0; l < s; ++l) {
-    st = run<KIND_I8_MOD>(M, N, K, RA + (size_t)l * M * K, RB + (size_t)l * N * K, CR + (size_t)l * cr_stride,
-                          nullptr, nullptr, stream, c.m[l]);
+    const lpgemm_status st = run<KIND_I8_MOD>(M, N, K, RA + (size_t)l * M * K, RB + (size_t)l * N * K,
+                                              CR + (size_t)l * cr_stride, nullptr, nullptr, stream, c.m[l]);
     if (st != LPGEMM_SUCCESS) return st;
   }
   // mod reduction, CRT reconstruction, undo scaling, write double
@@ -282,6 +286,64 @@ lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double* A, c
     if (e != hipSuccess) return LPGEMM_ERROR_LAUNCH;
   }
   return LPGEMM_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+lpgemm_status lpgemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A, const int8_t* B,
+                        int32_t* C, hipStream_t stream) {
+  return run<KIND_I8>(M, N, K, A, B, C, nullptr, nullptr, stream);
+}
+
+lpgemm_status lpgemm_i4(int64_t M, int64_t N, int64_t K, const uint8_t* A_packed,
+                        const uint8_t* B_packed, int32_t* C, hipStream_t stream) {
+  return run<KIND_I4>(M, N, K, A_packed, B_packed, C, nullptr, nullptr, stream);
+}
+
+int lpgemm_f64_emu_moduli(int64_t K, int bits) {
+  if (K < 0 || bits < 1 || bits > 53) return -1;
+  return f64emu_moduli(K, bits);
+}
+
+int64_t lpgemm_f64_emu_workspace(int64_t M, int64_t N, int64_t K, int bits) {
+  if (M < 0 || N < 0 || K < 0 || bits < 1 || bits > 53) return -1;
+  const int s = f64emu_moduli(K, bits);
+  if (s < 0) return -1;
+  return f64emu_layout(M, N, K, s).total;
+}
+
+lpgemm_status lpgemm_f64_emu(int64_t M, int64_t N, int64_t K, const double* A, const double* B,
+                             double* C, int bits, void* workspace, int64_t workspace_bytes,
+                             hipStream_t stream) {
+  int s = 0;
+  F64EmuLayout L{};
+  lpgemm_status st = f64emu_check(M, N, K, A, B, C, bits, s, L);
+  if (st != LPGEMM_SUCCESS || M == 0 || N == 0) return st;
+  if (!workspace) return LPGEMM_ERROR_INVALID_VALUE;
+  if (workspace_bytes < L.total) return LPGEMM_ERROR_INVALID_VALUE;
+  if (((uintptr_t)workspace & 255) != 0) return LPGEMM_ERROR_MISALIGNED;
+  DeviceInfo dev;
+  st = current_device(dev);
+  if (st != LPGEMM_SUCCESS) return st;
+  return f64emu_enqueue(M, N, K, A, B, C, bits, s, L, static_cast<uint8_t*>(workspace), stream);
+}
+
+lpgemm_status lpgemm_f64_emu_noalloc(int64_t M, int64_t N, int64_t K, const double* A, const double* B,
+                                     double* C, int bits, hipStream_t stream) {
+  int s = 0;
+  F64EmuLayout L{};
+  lpgemm_status st = f64emu_check(M, N, K, A, B, C, bits, s, L);
+  if (st != LPGEMM_SUCCESS || M == 0 || N == 0) return st;
+  if (L.total > LPGEMM_F64_EMU_NOALLOC_MAX_WORKSPACE) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  DeviceInfo dev;
+  st = current_device(dev);
+  if (st != LPGEMM_SUCCESS) return st;
+  void* ptr = nullptr;
+  st = scratch_address(ptr);
+  if (st != LPGEMM_SUCCESS) return st;
+  return f64emu_enqueue(M, N, K, A, B, C, bits, s, L, static_cast<uint8_t*>(ptr), stream);
 }
 
 lpgemm_status lpgemm_i8_kxn(int64_t M, int64_t N, int64_t K, const int8_t* A, const int8_t* B_kxn,

@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"lpgemm_i8", "lpgemm_i4", "lpgemm_f16", "lpgemm_i8_dequant",
                           "lpgemm_quantize_rows_f16", "lpgemm_w8a8_fused", "lpgemm_i4_to_e3m2",
                           "lpgemm_i4_e3m2",
-                          "lpgemm_i8_kxn", "lpgemm_f64_emu", "lpgemm_f64_emu_moduli",
+                          "lpgemm_i8_kxn", "lpgemm_f64_emu", "lpgemm_f64_emu_noalloc",
+                          "lpgemm_f64_emu_moduli",
                           "lpgemm_f64_emu_workspace",
                           "lpgemm_status_string", "lpgemm_version", "lpgemm_config_count",
                           "lpgemm_force_config"}
@@ -254,3 +255,23 @@ def test_f64_emu_validation(lib):
     assert f(4, 4, 64, FAKE, FAKE, FAKE, 53, WS, 100, None) == b.LPGEMM_ERROR_INVALID_VALUE  # too small
     assert f(4, 4, 64, MISALIGNED, FAKE, FAKE, 53, WS, big, None) == b.LPGEMM_ERROR_MISALIGNED
     assert f(4, 4, 64, FAKE, FAKE, FAKE, 53, WS + 16, big, None) == b.LPGEMM_ERROR_MISALIGNED
+
+
+def test_f64_emu_noalloc_validation(lib):
+    # the workspace entry point's checks, then the fixed scratch's limit,
+    # all on the host before any HIP call
+    f = lib.lpgemm_f64_emu_noalloc
+    assert f(-1, 4, 64, FAKE, FAKE, FAKE, 53, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 4, 64, FAKE, FAKE, FAKE, 0, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 4, 24, FAKE, FAKE, FAKE, 53, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    assert f(0, 4, 64, None, None, None, 53, None) == b.LPGEMM_SUCCESS   # empty
+    assert f(4, 4, 64, FAKE, FAKE, None, 53, None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert f(4, 4, 64, MISALIGNED, FAKE, FAKE, 53, None) == b.LPGEMM_ERROR_MISALIGNED
+    limit = 64 * 1024 * 1024
+    # the largest square size whose workspace fits, and the next multiple of 16
+    n = 16
+    while lib.lpgemm_f64_emu_workspace(n + 16, n + 16, n + 16, 53) <= limit:
+        n += 16
+    assert lib.lpgemm_f64_emu_workspace(n, n, n, 53) <= limit
+    assert f(n + 16, n + 16, n + 16, FAKE, FAKE, FAKE, 53, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    assert n >= 1024

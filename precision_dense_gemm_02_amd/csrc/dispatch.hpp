@@ -122,7 +122,14 @@ enum KernelCfg {
   CFG_256_S2_R128_PIN_E3M2 = 45, // E3M2 on configuration 0 with one MFMA pinned in front of each load
   CFG_256_S2_R128_PIN_KXN = 46,  // K x N B on configuration 0 with one MFMA pinned in front of each load
   CFG_256_S2_R128_PERSIST = 47,  // configuration 0 as a persistent grid of at most one workgroup per CU
-  CFG_COUNT = 48
+  // int4 ablations (the same kernels as the base configuration for the other kinds)
+  CFG_128_S2_R256_W4 = 48,       // configuration 36, int4 fragments read 32 packed bytes at a time
+  CFG_256_S2_R128_SX = 49,       // configuration 0, int4 expanded by sign extension (no x16 scaling)
+  CFG_256_S2_R128_W4 = 50,       // configuration 0, int4 fragments read 32 packed bytes at a time
+  CFG_128_S2_R256_SX = 51,       // configuration 36, int4 expanded by sign extension
+  CFG_256_S2_R128_PERSIST_SX = 52,  // configuration 47, int4 too, expanded by sign extension
+  CFG_256_S2_R128_PIN_SX = 53,   // configuration 0 with pinned loads, int4 too, expanded by sign extension
+  CFG_COUNT = 54
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -132,7 +139,10 @@ inline int stage_row_bytes(KernelCfg c) {
           c == CFG_128x64_S4_R64 || c == CFG_256x128_S4_R64 || c == CFG_128x64_S8_R64 ||
           c == CFG_256_S5_R64_NT || c == CFG_256_S4_R64_NT)
              ? 64
-             : ((c == CFG_128x64_S3_R256 || c == CFG_128_S2_R256) ? 256 : 128);
+             : ((c == CFG_128x64_S3_R256 || c == CFG_128_S2_R256 || c == CFG_128_S2_R256_W4 ||
+                 c == CFG_128_S2_R256_SX)
+                    ? 256
+                    : 128);
 }
 inline bool expands_int4_in_lds(KernelCfg c) { return c >= CFG_V1_256x256 && c <= CFG_V1_64x64; }
 
@@ -177,9 +187,12 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   if (big >= cu_count) return CFG_256_S2_R128;
   // 128 x 128 tiles: at 2048^3, two 256-byte stages for int8 and int4
   // (14.5 / 15.0 us against 15.4 / 15.7 us with four 64-byte stages), four
-  // 128-byte stages for fp16 (23.1 against 25.4 us)
+  // 128-byte stages for fp16 (23.1 against 25.4 us); int4 reads 32 packed
+  // bytes per fragment there, which removes the bank conflicts of 8-byte
+  // reads on 256-byte rows (1290 against 1248 TOP/s)
   const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
-  if (mid >= cu_count / 2) return kind == KIND_F16 ? CFG_128_S4_R128 : CFG_128_S2_R256;
+  if (mid >= cu_count / 2)
+    return kind == KIND_F16 ? CFG_128_S4_R128 : (kind == KIND_I4 ? CFG_128_S2_R256_W4 : CFG_128_S2_R256);
   return CFG_V1_64x64;
 }
 

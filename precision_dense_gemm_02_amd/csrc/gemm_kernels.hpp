@@ -129,6 +129,17 @@ __device__ __forceinline__ void expand_int4(uint32_t x, uint32_t& lo, uint32_t& 
   hi = x & 0xF0F0F0F0u;
 }
 
+// The sign-extending INT4 expansion (the same byte order, each byte holding
+// v itself, so no scaling is left for the epilogue): with c = n XOR 8 the
+// nibble's value plus 8, the byte c + 0x78 stays below 0x100 (no carry into
+// the next byte) and XOR 0x80 turns it into c - 8 modulo 256, the two's
+// complement byte of v.  Eight operations per eight nibbles against three.
+__device__ __forceinline__ void expand_int4_sx(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  const uint32_t t = x ^ 0x88888888u;
+  lo = ((t & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+  hi = (((t >> 4) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+}
+
 template <int KIND>
 struct KindTraits;
 template <>
@@ -560,6 +571,11 @@ struct RowLayout<64> {
 // into a 256-byte LDS sink), so that the chunk's lines are on their way to
 // the L2 one stage before the real loads ask for them.
 //
+// I4MODE (int4 only): bit 0, wide fragment reads: one ds_read_b128 takes 32
+// packed bytes (two MFMA K-steps) of a row, which feed two MFMAs per
+// accumulator block, instead of one ds_read_b64 per K-step; bit 1, the
+// sign-extending expansion (expand_int4_sx) instead of the x16-scaled one.
+//
 // PERSIST: a persistent grid (at most one workgroup per CU, launched with
 // the number of workgroups in gridDim.x) in which each workgroup walks its
 // tiles round by round, tile r·G + (its logical id) in round r, so that a
@@ -572,15 +588,22 @@ struct RowLayout<64> {
 // and keeps clear of the LDS stage those loads fill.  Two stages only.
 template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false,
           bool BKN = false, int LSTEPS = 0, bool NTC = false, int BSPLIT = 0, bool PF = false,
-          bool HIL = false, bool PERSIST = false>
+          bool HIL = false, bool PERSIST = false, int I4MODE = 0>
 __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
   constexpr bool I4 = KIND == KIND_I4;
   constexpr bool E3M2 = KIND == KIND_I4_E3M2;
-  // row bytes one MFMA K-step consumes: 32 packed int4 (16 B) expand to one
-  // int8 step; an E3M2 step is 64 values in two 32-byte groups
-  constexpr int kStepBytes = I4 ? 16 : (E3M2 ? 64 : 32);
+  constexpr bool W4 = I4 && (I4MODE & 1) != 0;   // wide int4 fragment reads
+  constexpr bool SX = I4 && (I4MODE & 2) != 0;   // sign-extending int4 expansion
+  static_assert(I4MODE == 0 || I4, "int4 knobs");
+  static_assert(!W4 || !HIL, "wide int4 reads keep the compiler's load placement");
+  // MFMAs per accumulator block per K-step
+  constexpr int kSub = W4 ? 2 : 1;
+  // row bytes one K-step consumes: 32 packed int4 (16 B) expand to one int8
+  // MFMA step (wide reads: 32 B, two MFMA steps); an E3M2 step is 64 values
+  // in two 32-byte groups
+  constexpr int kStepBytes = I4 ? (W4 ? 32 : 16) : (E3M2 ? 64 : 32);
   constexpr int KSTEPS = ROWB / kStepBytes;
   // the two fragment buffers alternate per K-step and the next stage's first
   // step reads into buffer 0 again, so a stage needs an even number of steps
@@ -751,7 +774,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   const int a_row_base = (wm * WTM) * ROWB;
   const int b_row_base = (BM + wn * WTN) * ROWB;
   auto frag_off = [&](int kk) -> int {
-    if constexpr (I4) return Layout::off(fr, kk) + fh * 8;       // 8 packed bytes
+    if constexpr (I4 && !W4) return Layout::off(fr, kk) + fh * 8;   // 8 packed bytes
     else if constexpr (E3M2) return Layout::off(fr, 4 * kk + 2 * fh);   // group, first chunk
     else return Layout::off(fr, 2 * kk + fh);                     // 16 bytes
   };
@@ -761,7 +784,8 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
 
   // E3M2 fragments are read straight into the eight-dword MFMA operand (of
   // which the FP6 format uses the low six)
-  using Raw = typename std::conditional<I4, i32x2_t, typename std::conditional<E3M2, i32x8, i32x4>::type>::type;
+  using Raw = typename std::conditional<I4 && !W4, i32x2_t,
+                                        typename std::conditional<E3M2, i32x8, i32x4>::type>::type;
   using Op = typename std::conditional<E3M2, i32x8, i32x4>::type;
   auto e3m2_frag = [](const uint8_t* p0, const uint8_t* p1) -> i32x8 {
     const i32x4 lo = *(const i32x4*)p0;
@@ -813,11 +837,18 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     }
   };
 
-  auto operand = [&](const Raw& r) -> Op {
+  // MFMA operand h (0 .. kSub-1) of a raw fragment
+  auto operand = [&](const Raw& r, int h = 0) -> Op {
     if constexpr (I4) {
       uint32_t lo0, hi0, lo1, hi1;
-      expand_int4((uint32_t)r.x, lo0, hi0);
-      expand_int4((uint32_t)r.y, lo1, hi1);
+      const uint32_t d0 = (uint32_t)r[2 * h], d1 = (uint32_t)r[2 * h + 1];
+      if constexpr (SX) {
+        expand_int4_sx(d0, lo0, hi0);
+        expand_int4_sx(d1, lo1, hi1);
+      } else {
+        expand_int4(d0, lo0, hi0);
+        expand_int4(d1, lo1, hi1);
+      }
       return i32x4{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
     } else {
       return r;
@@ -842,14 +873,18 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       else acc[i][j] = mfma<KIND>(a[i], b[j], acc[i][j]);
     }
   };
-  // ... on fragment buffer src, converted here (int4: expanded to int8)
+  // ... on fragment buffer src, converted here (int4: expanded to int8; wide
+  // int4 reads: both halves of each fragment, one MFMA each)
   auto compute = [&](int src, int first, int last) {
-    Op a[TM], b[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = operand(fa[src][i]);
+    for (int h = 0; h < kSub; ++h) {
+      Op a[TM], b[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = operand(fb[src][j]);
-    compute_ops(a, b, first, last);
+      for (int i = 0; i < TM; ++i) a[i] = operand(fa[src][i], h);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = operand(fb[src][j], h);
+      compute_ops(a, b, first, last);
+    }
   };
 
   constexpr int kMfma = TM * TN;
@@ -864,7 +899,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
 #pragma unroll
     for (int x = 0; x < kMfma; ++x) {
       if (x >= mfmas) break;
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, kSub, 0);               // MFMA
       if (x < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       if (x < loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
     }
@@ -957,7 +992,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       return __builtin_bit_cast(uint32_t, (float)acc[i][j][e]);
     } else if constexpr (E3M2) {
       return (uint32_t)(int32_t)acc[i][j][e];   // an integer below 2^24: exact
-    } else if constexpr (KIND == KIND_I4) {
+    } else if constexpr (KIND == KIND_I4 && !SX) {
       return (uint32_t)(acc[i][j][e] >> 8);   // undo the 16 x 16 scaling
     } else {
       return (uint32_t)acc[i][j][e];
@@ -1029,10 +1064,14 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
         const int rl = row0 + half * kEpiRows + lane;
         if (lane < kEpiRows && rl < p.M) rs_half = p.row_scale[rl];
       }
-#pragma unroll
-      for (int r0 = 0; r0 < kEpiRows; r0 += kRowsPerStore) {
-        const int r = r0 + lane / kLanesPerRow;
-        i32x4 v = *(const i32x4*)(stage_out + r * kEpiPitch + c_lane * 4);
+      // the staged rows of this pass, kRowsPerStore per read: a group of
+      // reads is issued back to back and only then stored, so that the
+      // reads' LDS latency is paid once per group rather than once per row
+      constexpr int kReadsPerPass = kEpiRows / kRowsPerStore;
+      constexpr int kGroup = kReadsPerPass < 16 ? kReadsPerPass : 16;
+      static_assert(kReadsPerPass % kGroup == 0, "read groups");
+      const int gcol = col0 + c_lane;
+      auto scaled = [&](i32x4 v, int r0) -> i32x4 {
         if constexpr (KIND == KIND_I8_DEQUANT) {
           // ((float)acc * row_scale) * col_scale, each product rounded once
           float rs = 0.f;
@@ -1050,16 +1089,56 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
             v[x] = __builtin_bit_cast(int, t);
           }
         }
-        const int grow = row0 + half * kEpiRows + r;
-        const int gcol = col0 + c_lane;
-        uint32_t* dst = (uint32_t*)p.C + (size_t)grow * p.N + gcol;
-        if (full) {
-          if constexpr (NTC) __builtin_nontemporal_store(v, (i32x4*)dst);
-          else *(i32x4*)dst = v;
-        } else if (grow < p.M) {
+        return v;
+      };
+      if constexpr (I4) {
+        // int4: one row at a time (its main loop already holds 256 VGPRs)
 #pragma unroll
-          for (int x = 0; x < 4; ++x)
-            if (gcol + x < p.N) dst[x] = (uint32_t)v[x];
+        for (int r0 = 0; r0 < kEpiRows; r0 += kRowsPerStore) {
+          const int r = r0 + lane / kLanesPerRow;
+          i32x4 v = *(const i32x4*)(stage_out + r * kEpiPitch + c_lane * 4);
+          const int grow = row0 + half * kEpiRows + r;
+          uint32_t* dst = (uint32_t*)p.C + (size_t)grow * p.N + gcol;
+          if (full) {
+            if constexpr (NTC) __builtin_nontemporal_store(v, (i32x4*)dst);
+            else *(i32x4*)dst = v;
+          } else if (grow < p.M) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+              if (gcol + x < p.N) dst[x] = (uint32_t)v[x];
+          }
+        }
+      } else if (full) {
+#pragma unroll
+        for (int g = 0; g < kReadsPerPass; g += kGroup) {
+          i32x4 v[kGroup];
+#pragma unroll
+          for (int q = 0; q < kGroup; ++q) {
+            const int r = (g + q) * kRowsPerStore + lane / kLanesPerRow;
+            v[q] = *(const i32x4*)(stage_out + r * kEpiPitch + c_lane * 4);
+          }
+#pragma unroll
+          for (int q = 0; q < kGroup; ++q) {
+            const int r0 = (g + q) * kRowsPerStore;
+            const i32x4 w = scaled(v[q], r0);
+            const int grow = row0 + half * kEpiRows + r0 + lane / kLanesPerRow;
+            i32x4* dst = (i32x4*)((uint32_t*)p.C + (size_t)grow * p.N + gcol);
+            if constexpr (NTC) __builtin_nontemporal_store(w, dst);
+            else *dst = w;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r0 = 0; r0 < kEpiRows; r0 += kRowsPerStore) {
+          const int r = r0 + lane / kLanesPerRow;
+          const i32x4 v = scaled(*(const i32x4*)(stage_out + r * kEpiPitch + c_lane * 4), r0);
+          const int grow = row0 + half * kEpiRows + r;
+          uint32_t* dst = (uint32_t*)p.C + (size_t)grow * p.N + gcol;
+          if (grow < p.M) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+              if (gcol + x < p.N) dst[x] = (uint32_t)v[x];
+          }
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next half overwrites

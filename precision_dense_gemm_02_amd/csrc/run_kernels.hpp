@@ -54,6 +54,8 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   // MI355X: int8 2306 against 2271 TOP/s, fp16 1221 against 1182 TFLOP/s),
   // except for int4, whose expanded operands would then spill
   constexpr bool kPinLoads = KIND != KIND_I4;
+  // an int4 knob (gemm_v3's I4MODE), 0 for the other kinds
+  constexpr auto kI4 = [](int mode) constexpr { return KIND == KIND_I4 ? mode : 0; };
 
   if constexpr (BKN) {
     switch (cfg) {
@@ -104,6 +106,31 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launch_persistent<256, 256>(
             (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads, true>,
             args, 256, stream, dev.cu_count);
+    // int4 knobs; every other kind runs the base configuration's kernel
+    case CFG_128_S2_R256_W4:
+      return launch<128, 128>(
+          (const void*)&gemm_v3<KIND, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, kI4(1)>,
+          args, 256, stream);
+    case CFG_128_S2_R256_SX:
+      return launch<128, 128>(
+          (const void*)&gemm_v3<KIND, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, kI4(2)>,
+          args, 256, stream);
+    case CFG_256_S2_R128_SX:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads, false, kI4(2)>,
+          args, 256, stream);
+    case CFG_256_S2_R128_W4:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads, false, kI4(1)>,
+          args, 256, stream);
+    case CFG_256_S2_R128_PERSIST_SX:
+      return launch_persistent<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads, true, kI4(2)>,
+          args, 256, stream, dev.cu_count);
+    case CFG_256_S2_R128_PIN_SX:
+      return launch<256, 256>(
+          (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, true, false, kI4(2)>,
+          args, 256, stream);
     case CFG_256_S4_R64:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 4, 64>, args, 256, stream);
     case CFG_256_S3_R64:

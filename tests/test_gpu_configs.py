@@ -146,12 +146,15 @@ def test_persistent_i8_rounds(M, N, K):
     np.testing.assert_array_equal(out.cpu().numpy()[rows], oracle.gemm_i8(p.a, p.b_t, rows=rows))
 
 
+@pytest.mark.parametrize("cfg", [PERSIST_CFG, 52])
 @pytest.mark.parametrize("K", [32, 544, 800])
-def test_persistent_i4_rounds(K):
+def test_persistent_i4_rounds(K, cfg):
+    # configuration 52 is the persistent grid for int4 as well (sign-extending
+    # expansion); 47 runs configuration 0 for int4
     M, N = 4100, 4100
-    print("[case] persistent i4", M, N, K, flush=True)
+    print("[case] persistent i4", cfg, M, N, K, flush=True)
     p = inputs.int4_problem(M, N, K, seed=K)
-    prev = lp.force_config(PERSIST_CFG)
+    prev = lp.force_config(cfg)
     try:
         out = lp.gemm_i4(_dev(p.a_packed), _dev(p.b_packed), K)
         torch.cuda.synchronize()

@@ -49,8 +49,38 @@ def _jobs() -> int:
     return max(1, min(n, 16, int(os.environ.get("MAX_JOBS", "16"))))
 
 
+TEST_HIP = os.path.join(ROOT, "tests", "hip")
+
+
+def test_probe_sources() -> list:
+    """HIP sources of the test suite's device probes (each becomes a shared
+    library next to it; the product library never loads them)."""
+    return sorted(glob.glob(os.path.join(TEST_HIP, "*.hip")))
+
+
+def _build_test_probe(src: str, verbose: bool = False) -> str:
+    out = os.path.join(os.path.dirname(src), "lib" + os.path.basename(src)[:-4] + ".so")
+    cmd = [HIPCC, *FLAGS, "-shared", src, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)} ({r.returncode}):\n{_filter(r.stderr)}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     srcs = sources()
+    with ThreadPoolExecutor(max_workers=2) as outer:
+        probes = [outer.submit(_build_test_probe, p, verbose) for p in test_probe_sources()]
+        lib = _build_library(srcs, verbose)
+        for f in probes:
+            f.result()
+    return lib
+
+
+def _build_library(srcs: list, verbose: bool) -> str:
     with tempfile.TemporaryDirectory(prefix="lpgemm_build_") as tmpdir:
         def compile_one(src):
             obj = os.path.join(tmpdir, os.path.basename(src)[:-4] + ".o")

@@ -129,7 +129,8 @@ enum KernelCfg {
   CFG_128_S2_R256_SX = 51,       // configuration 36, int4 expanded by sign extension
   CFG_256_S2_R128_PERSIST_SX = 52,  // configuration 47, int4 too, expanded by sign extension
   CFG_256_S2_R128_PIN_SX = 53,   // configuration 0 with pinned loads, int4 too, expanded by sign extension
-  CFG_COUNT = 54
+  CFG_REF = 54,                  // the reference kernel: one unswizzled LDS stage, nothing tuned (gemm_ref)
+  CFG_COUNT = 55
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged

@@ -1196,6 +1196,111 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Reference kernel: the same contraction with nothing tuned.  One LDS stage
+// (load, barrier, contract, barrier), operand rows stored unswizzled, plain
+// per-lane global loads and 4-byte stores, a 128 x 128 tile of four 64 x 64
+// wave quadrants.  It feeds each accumulator the same K-steps, in the same
+// order and with the same lane-to-k assignment as the pipelined kernels
+// (lane l: row l % 32 of a 32-row block, bytes 16 (l / 32) .. + 15 of a
+// 32-byte K-step; packed int4: bytes 8 (l / 32) .. + 7 of a 16-byte step), so
+// for fp16 its result must equal theirs bit for bit: the bring-up version
+// against which the swizzled, multi-stage kernels are checked.
+template <int KIND>
+__global__ __launch_bounds__(256) void gemm_ref(GemmArgs p) {
+  using Acc = typename KindTraits<KIND>::Acc;
+  static_assert(KIND == KIND_I8 || KIND == KIND_I4 || KIND == KIND_F16 || KIND == KIND_I8_DEQUANT, "kinds");
+  constexpr bool I4 = KIND == KIND_I4;
+  constexpr int BM = 128, BN = 128, ROWB = 128;      // LDS bytes per operand row
+  constexpr int kStep = I4 ? 16 : 32;                // row bytes one MFMA K-step consumes
+  constexpr int TM = 2, TN = 2;                      // 32 x 32 blocks per wave
+  __shared__ __attribute__((aligned(16))) uint8_t sa[BM * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t sb[BN * ROWB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int fr = lane & 31, fh = lane >> 5;
+
+  Acc acc[TM][TN];
+  for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j)
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  for (int ks = 0; ks < p.k_stages; ++ks) {
+    const int kb0 = ks * ROWB;
+    __syncthreads();   // every wave is done with the previous stage
+    // 128 rows x 8 chunks of 16 bytes per operand: four chunks per thread
+    for (int c = tid; c < BM * (ROWB / 16); c += 256) {
+      const int r = c / (ROWB / 16), col = (c % (ROWB / 16)) * 16;
+      i32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+      if (m0 + r < p.M && kb0 + col < p.row_bytes)
+        va = *(const i32x4*)(p.A + (size_t)(m0 + r) * p.row_bytes + kb0 + col);
+      if (n0 + r < p.N && kb0 + col < p.row_bytes)
+        vb = *(const i32x4*)(p.B + (size_t)(n0 + r) * p.row_bytes + kb0 + col);
+      *(i32x4*)(sa + r * ROWB + col) = va;
+      *(i32x4*)(sb + r * ROWB + col) = vb;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < ROWB / kStep; ++kk) {
+      i32x4 fa[TM], fb[TN];
+      for (int i = 0; i < TM; ++i) {
+        const uint8_t* ra = sa + (wm * 64 + i * 32 + fr) * ROWB + kk * kStep;
+        if constexpr (I4) {
+          uint32_t lo0, hi0, lo1, hi1;
+          const i32x2_t x = *(const i32x2_t*)(ra + 8 * fh);
+          expand_int4((uint32_t)x.x, lo0, hi0);
+          expand_int4((uint32_t)x.y, lo1, hi1);
+          fa[i] = i32x4{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
+        } else {
+          fa[i] = *(const i32x4*)(ra + 16 * fh);
+        }
+      }
+      for (int j = 0; j < TN; ++j) {
+        const uint8_t* rb = sb + (wn * 64 + j * 32 + fr) * ROWB + kk * kStep;
+        if constexpr (I4) {
+          uint32_t lo0, hi0, lo1, hi1;
+          const i32x2_t x = *(const i32x2_t*)(rb + 8 * fh);
+          expand_int4((uint32_t)x.x, lo0, hi0);
+          expand_int4((uint32_t)x.y, lo1, hi1);
+          fb[j] = i32x4{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
+        } else {
+          fb[j] = *(const i32x4*)(rb + 16 * fh);
+        }
+      }
+      for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma<KIND>(fa[i], fb[j], acc[i][j]);
+    }
+  }
+
+  // element e of lane l in a 32 x 32 block: row 8 (e / 4) + 4 (l / 32) + e % 4,
+  // column l % 32
+  for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + fr;
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+        if (row >= p.M || col >= p.N) continue;
+        const size_t idx = (size_t)row * p.N + col;
+        const auto v = acc[i][j][e];
+        if constexpr (KIND == KIND_F16) {
+          ((float*)p.C)[idx] = v;
+        } else if constexpr (I4) {
+          ((int32_t*)p.C)[idx] = v >> 8;   // undo the 16 x 16 scaling
+        } else if constexpr (KIND == KIND_I8_DEQUANT) {
+          float t = (float)v;
+          t = t * p.row_scale[row];
+          t = t * p.col_scale[col];
+          ((float*)p.C)[idx] = t;
+        } else {
+          ((int32_t*)p.C)[idx] = v;
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Eight-wave ping-pong kernel.
 //
 // A 256 x 256 tile is split into eight 128 x 64 wave tiles; waves w and w+4

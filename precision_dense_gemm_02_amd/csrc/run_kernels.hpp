@@ -131,6 +131,8 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<256, 256>(
           (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, true, false, kI4(2)>,
           args, 256, stream);
+    case CFG_REF:
+      return launch<128, 128>((const void*)&gemm_ref<KIND>, args, 256, stream);
     case CFG_256_S4_R64:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 4, 64>, args, 256, stream);
     case CFG_256_S3_R64:

@@ -275,3 +275,13 @@ def test_f64_emu_noalloc_validation(lib):
     assert lib.lpgemm_f64_emu_workspace(n, n, n, 53) <= limit
     assert f(n + 16, n + 16, n + 16, FAKE, FAKE, FAKE, 53, None) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
     assert n >= 1024
+
+
+def test_layout_probe_library_exports():
+    # the device probes of tests/test_gpu_layout_probes.py (test
+    # infrastructure, built by the same build step), loadable without a GPU
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "liblayout_probes.so")
+    probes = ctypes.CDLL(path)
+    for name in ("probe_mfma_i8", "probe_mfma_f16", "probe_mfma_e3m2", "probe_ds_read_tr8", "probe_lds_dma"):
+        assert hasattr(probes, name), name

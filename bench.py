@@ -507,9 +507,9 @@ def platform_library(steps: int, warmup: int, settle_s: float, n: int = 8192) ->
 # the kernel each square workload runs at 8192 (the persistent configuration
 # 47 for int8 and fp16, configuration 0 for int4)
 TRAFFIC_KERNELS = {
-    "i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0>(lpgemm::GemmArgs)",
-    "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false, false, 0>(lpgemm::GemmArgs)",
-    "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0>(lpgemm::GemmArgs)"}
+    "i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false>(lpgemm::GemmArgs)",
+    "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false, false, 0, false>(lpgemm::GemmArgs)",
+    "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false>(lpgemm::GemmArgs)"}
 
 
 def _median_counter(path: str, kernel: str, counter: str) -> float:

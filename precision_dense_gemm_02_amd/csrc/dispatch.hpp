@@ -130,7 +130,11 @@ enum KernelCfg {
   CFG_256_S2_R128_PERSIST_SX = 52,  // configuration 47, int4 too, expanded by sign extension
   CFG_256_S2_R128_PIN_SX = 53,   // configuration 0 with pinned loads, int4 too, expanded by sign extension
   CFG_REF = 54,                  // the reference kernel: one unswizzled LDS stage, nothing tuned (gemm_ref)
-  CFG_COUNT = 55
+  CFG_STREAM_128x64 = 55,        // short M: 128 x 64 tiles, A (3 stages) and B (10 stages) in separate rings
+  CFG_STREAM_128x64_B14 = 56,    // ... B in 14 stages (A in 2)
+  CFG_STREAM_64x64 = 57,         // ... 64 x 64 tiles, A 3 stages, B 14 stages
+  CFG_256_S2_R128_EARLY = 58,    // configuration 0 with half of each stage's loads issued one K-step earlier
+  CFG_COUNT = 59
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged

@@ -576,6 +576,12 @@ struct RowLayout<64> {
 // accumulator block, instead of one ds_read_b64 per K-step; bit 1, the
 // sign-extending expansion (expand_int4_sx) instead of the x16-scaled one.
 //
+// EARLY (with pinned loads, two stages): the first half of stage s + 2's
+// loads go out in stage s's last K-step, right after the barrier that frees
+// stage s's buffer, one behind each MFMA left in that K-step; the second
+// half in stage s + 1's first K-step.  The loads then leave about a K-step
+// earlier than with LSTEPS = 2.
+//
 // PERSIST: a persistent grid (at most one workgroup per CU, launched with
 // the number of workgroups in gridDim.x) in which each workgroup walks its
 // tiles round by round, tile r·G + (its logical id) in round r, so that a
@@ -588,7 +594,7 @@ struct RowLayout<64> {
 // and keeps clear of the LDS stage those loads fill.  Two stages only.
 template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false,
           bool BKN = false, int LSTEPS = 0, bool NTC = false, int BSPLIT = 0, bool PF = false,
-          bool HIL = false, bool PERSIST = false, int I4MODE = 0>
+          bool HIL = false, bool PERSIST = false, int I4MODE = 0, bool EARLY = false>
 __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
@@ -895,6 +901,11 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   constexpr int kLoadSteps = LSTEPS > 0 ? LSTEPS : (KSTEPS > 1 ? KSTEPS - 1 : 1);
   static_assert(kLoadSteps < KSTEPS || KSTEPS == 1, "loads end before the stage's last K-step");
   constexpr int kLoadsPerStep = (kSlots + kLoadSteps - 1) / kLoadSteps;
+  static_assert(!EARLY || (STAGES == 2 && HIL && !kOnce && !PERSIST && !PF && !BKN && !SPLIT), "early loads");
+  // early loads: slots t < kHead of a stage go out in the stage two before
+  // it (after its barrier), the others in the stage before it (K-step 0)
+  constexpr int kHead = EARLY ? kSlots / 2 : 0;
+  static_assert(!EARLY || kHead <= kMfma - kSplit, "one MFMA in front of each early load");
   auto interleave = [&](int mfmas, int reads, int loads) {
 #pragma unroll
     for (int x = 0; x < kMfma; ++x) {
@@ -915,7 +926,11 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
 #pragma unroll
       for (int t = 0; t < kSlots; ++t) issue_load(t, s);
     if constexpr (PF) issue_prefetch(STAGES - 1);
-    wait_vmcnt<(STAGES - 2) * kSlots + kPf>();   // own loads of stage 0
+    if constexpr (EARLY) {
+#pragma unroll
+      for (int t = 0; t < kHead; ++t) issue_load(t, 1);   // stage 1's early half
+    }
+    wait_vmcnt<(STAGES - 2) * kSlots + kPf + kHead>();   // own loads of stage 0
     block_barrier();                             // everyone's
     read_frags(0, 0, 0);
   }
@@ -940,10 +955,10 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       };
       int nl = 0;
       int pre = 0;   // MFMAs already issued in front of this K-step's loads
-      if (kk < kLoadSteps) {
+      if (EARLY ? kk == 0 : kk < kLoadSteps) {
 #pragma unroll
         for (int t = 0; t < kSlots; ++t) {
-          if (t / kLoadsPerStep != kk) continue;
+          if (EARLY ? t < kHead : t / kLoadsPerStep != kk) continue;
           if constexpr (HIL) {
             if (pre < (kk + 1 < KSTEPS ? kMfma : kSplit)) {
               mm(pre, pre + 1);
@@ -976,8 +991,21 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
         wait_lgkmcnt0();                       // own reads of stage s done
         block_barrier();                       // ... everyone's
         read_frags(s + 1, 0, dst);
-        mm(kSplit, kMfma);
-        interleave(kMfma - kSplit, kReads, 0);
+        if constexpr (EARLY) {
+          // stage s's buffer is free: the early half of stage s + 2, one
+          // load behind each of the K-step's remaining MFMAs
+#pragma unroll
+          for (int t = 0; t < kHead; ++t) {
+            mm(kSplit + t, kSplit + t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_load(t, s + 2);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        mm(kSplit + kHead, kMfma);
+        // (early loads: the next stage's first fragment reads went out before
+        // the pinned loads)
+        interleave(kMfma - kSplit - kHead, EARLY ? 0 : kReads, 0);
       }
     }
   }
@@ -1193,6 +1221,179 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
   }
   }   // tiles
+}
+
+// ---------------------------------------------------------------------------
+// Weight-streaming kernel for short M (the LLM projection's 128-token band).
+//
+// With M <= BM the whole of A is a few hundred KiB that every workgroup
+// needs, while each workgroup streams its own BN rows of B from HBM, once.
+// How fast B arrives is set by how many of its bytes each CU keeps in
+// flight: a ring whose stages hold A and B together (the tiled kernels)
+// spends two thirds of the LDS on A, which comes from L2 at short latency,
+// and leaves B two stages (32 KiB) in flight.  Here A and B get rings of
+// their own, of different depths, filled by different waves: the vector
+// memory counter retires a wave's loads in issue order, so one wave cannot
+// wait for a near A stage without also waiting for the far B stages issued
+// before it.  Wave 4 loads A (SA stages of BM rows); waves 0-3 load B (SB
+// stages of BN rows) and compute, a 2 x 2 arrangement of (BM/2) x (BN/2)
+// quadrants.  One barrier per stage: every wave first waits for its own
+// loads of the next stage and for its fragment reads of this one, so past
+// the barrier the next stage is whole and this one's buffers are free.  The
+// accumulators are stored straight to C (4-byte stores, masked at the
+// edges): the tile is small next to the B panel it streams.
+template <int KIND, int BM, int BN, int SA, int SB>
+__global__ __launch_bounds__(320) void gemm_stream(GemmArgs p) {
+  using Acc = typename KindTraits<KIND>::Acc;
+  static_assert(KIND == KIND_I8 || KIND == KIND_I8_DEQUANT || KIND == KIND_F16 || KIND == KIND_I4, "kinds");
+  constexpr bool I4 = KIND == KIND_I4;
+  using Layout = RowLayout<128>;
+  // a K-step: 32 row bytes (int4: 16 packed bytes, expanded to one int8 step)
+  constexpr int ROWB = 128, KSTEPS = ROWB / (I4 ? 16 : 32);
+  constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "quadrants");
+  constexpr int kStageA = BM * ROWB, kStageB = BN * ROWB;
+  constexpr int kLoadsA = BM / 8;          // 1 KiB loads of an A stage, all by wave 4
+  constexpr int kLoadsB = BN / 8 / 4;      // ... of a B stage, per compute wave
+  static_assert(kLoadsB >= 1 && (BN / 8) % 4 == 0, "B loads per wave");
+  static_assert((SA - 2) * kLoadsA <= 63 && (SB - 2) * kLoadsB <= 63 && SA >= 2 && SB >= 2, "vmcnt range");
+  constexpr int kBaseB = SA * kStageA;
+  static_assert(kBaseB + SB * kStageB <= 160 * 1024, "LDS");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBaseB + SB * kStageB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const i32x4 rsrc_a = make_rsrc(p.A + (size_t)m0 * p.row_bytes, min(BM, p.M - m0) * p.row_bytes);
+  const i32x4 rsrc_b = make_rsrc(p.B + (size_t)n0 * p.row_bytes, min(BN, p.N - n0) * p.row_bytes);
+  const uint32_t smem_lds = lds_address(smem);
+  const int nks = p.k_stages;
+  const bool loader = wave == 4;
+
+  // load g of a stage fills rows 8g .. 8g + 7: lane l writes row 8g + l / 8
+  // at chunk position l % 8, so it fetches the global chunk whose swizzled
+  // position that is
+  auto chunk_of = [&](int g, uint32_t& off, uint32_t& col) {
+    const int row = 8 * g + lane / 8;
+    const int c = Layout::pos(row, lane % 8);
+    off = (uint32_t)row * (uint32_t)p.row_bytes + c * 16;
+    col = c * 16;
+  };
+  auto issue = [&](int s) {
+    const uint32_t kbyte = (uint32_t)s * ROWB;
+    if (loader) {
+#pragma unroll
+      for (int g = 0; g < kLoadsA; ++g) {
+        uint32_t off, col;
+        chunk_of(g, off, col);
+        lds_dma_16(rsrc_a, smem_lds + (s % SA) * kStageA + g * 1024,
+                   kbyte + col < (uint32_t)p.row_bytes ? off + kbyte : kOutOfRange);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kLoadsB; ++t) {
+        const int g = wave * kLoadsB + t;
+        uint32_t off, col;
+        chunk_of(g, off, col);
+        lds_dma_16(rsrc_b, smem_lds + kBaseB + (s % SB) * kStageB + g * 1024,
+                   kbyte + col < (uint32_t)p.row_bytes ? off + kbyte : kOutOfRange);
+      }
+    }
+  };
+  // each wave waits for its own loads of stage s + 1 (the loads of the
+  // stages after it stay in flight), then for its fragment reads, then meets
+  // the others
+  auto stage_end = [&]() {
+    if (loader) wait_vmcnt<(SA - 2) * kLoadsA>();
+    else wait_vmcnt<(SB - 2) * kLoadsB>();
+    wait_lgkmcnt0();
+    block_barrier();
+  };
+
+  const int wm = (wave >> 1) & 1, wn = wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+  Acc acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  if (nks > 0) {
+    const int pre = loader ? SA - 1 : SB - 1;
+    for (int s = 0; s < pre; ++s) issue(s);
+    if (loader) wait_vmcnt<(SA - 2) * kLoadsA>();
+    else wait_vmcnt<(SB - 2) * kLoadsB>();
+    block_barrier();   // stage 0 of A and B has landed
+  }
+  for (int s = 0; s < nks; ++s) {
+    // the stage that reuses the buffers stage s - 1 released at the last barrier
+    issue(s + (loader ? SA : SB) - 1);
+    if (!loader) {
+      const uint8_t* a_base = smem + (s % SA) * kStageA + (wm * WTM) * ROWB;
+      const uint8_t* b_base = smem + kBaseB + (s % SB) * kStageB + (wn * WTN) * ROWB;
+      auto frag = [&](const uint8_t* p0) -> i32x4 {
+        if constexpr (I4) {
+          const i32x2_t x = *(const i32x2_t*)p0;
+          uint32_t lo0, hi0, lo1, hi1;
+          expand_int4((uint32_t)x.x, lo0, hi0);
+          expand_int4((uint32_t)x.y, lo1, hi1);
+          return i32x4{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
+        } else {
+          return *(const i32x4*)p0;
+        }
+      };
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int off = I4 ? Layout::off(fr, kk) + 8 * fh : Layout::off(fr, 2 * kk + fh);
+        i32x4 fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = frag(a_base + i * 32 * ROWB + off);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = frag(b_base + j * 32 * ROWB + off);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma<KIND>(fa[i], fb[j], acc[i][j]);
+      }
+    }
+    stage_end();
+  }
+  wait_vmcnt<0>();   // loads past the last stage (zeros nobody reads)
+  if (loader) return;
+
+  // element e of lane l in a 32 x 32 block: row 8 (e / 4) + 4 (l / 32) + e % 4,
+  // column l % 32
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + fr;
+      float cs = 0.f;
+      if constexpr (KIND == KIND_I8_DEQUANT) cs = col < p.N ? p.col_scale[col] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+        if (row >= p.M || col >= p.N) continue;
+        const size_t idx = (size_t)row * p.N + col;
+        if constexpr (KIND == KIND_F16) {
+          ((float*)p.C)[idx] = acc[i][j][e];
+        } else if constexpr (KIND == KIND_I8_DEQUANT) {
+          float t = (float)acc[i][j][e];
+          t = t * p.row_scale[row];
+          t = t * cs;
+          ((float*)p.C)[idx] = t;
+        } else if constexpr (I4) {
+          ((int32_t*)p.C)[idx] = acc[i][j][e] >> 8;   // undo the 16 x 16 scaling
+        } else {
+          ((int32_t*)p.C)[idx] = acc[i][j][e];
+        }
+      }
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -131,6 +131,22 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<256, 256>(
           (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, true, false, kI4(2)>,
           args, 256, stream);
+    case CFG_STREAM_128x64:
+      return launch<128, 64>((const void*)&gemm_stream<KIND, 128, 64, 3, 10>, args, 320, stream);
+    case CFG_STREAM_128x64_B14:
+      return launch<128, 64>((const void*)&gemm_stream<KIND, 128, 64, 2, 14>, args, 320, stream);
+    case CFG_STREAM_64x64:
+      return launch<64, 64>((const void*)&gemm_stream<KIND, 64, 64, 3, 14>, args, 320, stream);
+    case CFG_256_S2_R128_EARLY:
+      // int4 keeps configuration 0 (no pinned loads, see kPinLoads)
+      if constexpr (KIND == KIND_I4)
+        return launch<256, 256>(
+            (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads>, args, 256,
+            stream);
+      else
+        return launch<256, 256>(
+            (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, true, false, 0, true>,
+            args, 256, stream);
     case CFG_REF:
       return launch<128, 128>((const void*)&gemm_ref<KIND>, args, 256, stream);
     case CFG_256_S4_R64:

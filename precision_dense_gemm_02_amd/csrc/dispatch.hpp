@@ -134,7 +134,8 @@ enum KernelCfg {
   CFG_STREAM_128x64_B14 = 56,    // ... B in 14 stages (A in 2)
   CFG_STREAM_64x64 = 57,         // ... 64 x 64 tiles, A 3 stages, B 14 stages
   CFG_256_S2_R128_EARLY = 58,    // configuration 0 with half of each stage's loads issued one K-step earlier
-  CFG_COUNT = 59
+  CFG_128_S2_R256_BIAS = 59,     // configuration 36, int4 expanded biased (u = v + 8) with sum corrections
+  CFG_COUNT = 60
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -145,7 +146,7 @@ inline int stage_row_bytes(KernelCfg c) {
           c == CFG_256_S5_R64_NT || c == CFG_256_S4_R64_NT)
              ? 64
              : ((c == CFG_128x64_S3_R256 || c == CFG_128_S2_R256 || c == CFG_128_S2_R256_W4 ||
-                 c == CFG_128_S2_R256_SX)
+                 c == CFG_128_S2_R256_SX || c == CFG_128_S2_R256_BIAS)
                     ? 256
                     : 128);
 }

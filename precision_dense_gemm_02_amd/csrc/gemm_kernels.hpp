@@ -574,7 +574,14 @@ struct RowLayout<64> {
 // I4MODE (int4 only): bit 0, wide fragment reads: one ds_read_b128 takes 32
 // packed bytes (two MFMA K-steps) of a row, which feed two MFMAs per
 // accumulator block, instead of one ds_read_b64 per K-step; bit 1, the
-// sign-extending expansion (expand_int4_sx) instead of the x16-scaled one.
+// sign-extending expansion (expand_int4_sx) instead of the x16-scaled one;
+// bit 2, the biased expansion: XOR 0x8 turns every nibble into u = v + 8 in
+// [0, 15], which needs no sign handling (lo = t & 0x0F0F0F0F, hi = (t >> 4)
+// & 0x0F0F0F0F), and the MFMA sums u_a u_b; since (u_a - 8)(u_b - 8) =
+// u_a u_b - 8 u_a - 8 u_b + 64, the epilogue subtracts 8 times each row's
+// and each column's sum of u (kept per lane with v_dot8_u32_u4 against
+// 0x11111111 as the fragments pass) and adds 64 per k summed.  Zero padding
+// past K reads as v = 0, u = 8, and contributes 64 - 64 - 64 + 64 = 0.
 //
 // EARLY (with pinned loads, two stages): the first half of stage s + 2's
 // loads go out in stage s's last K-step, right after the barrier that frees
@@ -602,7 +609,9 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   constexpr bool E3M2 = KIND == KIND_I4_E3M2;
   constexpr bool W4 = I4 && (I4MODE & 1) != 0;   // wide int4 fragment reads
   constexpr bool SX = I4 && (I4MODE & 2) != 0;   // sign-extending int4 expansion
+  constexpr bool BIAS = I4 && (I4MODE & 4) != 0; // biased int4 expansion with sum corrections
   static_assert(I4MODE == 0 || I4, "int4 knobs");
+  static_assert(!BIAS || (!SX && !PERSIST && !HIL), "one expansion; the biased one on the plain kernel");
   static_assert(!W4 || !HIL, "wide int4 reads keep the compiler's load placement");
   // MFMAs per accumulator block per K-step
   constexpr int kSub = W4 ? 2 : 1;
@@ -851,6 +860,12 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       if constexpr (SX) {
         expand_int4_sx(d0, lo0, hi0);
         expand_int4_sx(d1, lo1, hi1);
+      } else if constexpr (BIAS) {
+        const uint32_t t0 = d0 ^ 0x88888888u, t1 = d1 ^ 0x88888888u;
+        lo0 = t0 & 0x0F0F0F0Fu;
+        hi0 = (t0 >> 4) & 0x0F0F0F0Fu;
+        lo1 = t1 & 0x0F0F0F0Fu;
+        hi1 = (t1 >> 4) & 0x0F0F0F0Fu;
       } else {
         expand_int4(d0, lo0, hi0);
         expand_int4(d1, lo1, hi1);
@@ -868,6 +883,28 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  // biased int4: per lane, the running sum of u over its row (A) or column
+  // (B) of each block and its half of every K-step
+  uint32_t usum_a[TM], usum_b[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) usum_a[i] = 0;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) usum_b[j] = 0;
+  auto add_usums = [&](int src) {
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+          usum_a[i] = __builtin_amdgcn_udot8((uint32_t)fa[src][i][d] ^ 0x88888888u, 0x11111111u, usum_a[i], false);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+          usum_b[j] = __builtin_amdgcn_udot8((uint32_t)fb[src][j][d] ^ 0x88888888u, 0x11111111u, usum_b[j], false);
+    }
+  };
 
   // MFMAs first .. last-1 of a K-step on operands already in MFMA form
   auto compute_ops = [&](const Op (&a)[TM], const Op (&b)[TN], int first, int last) {
@@ -942,6 +979,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       const int src = kk & 1, dst = src ^ 1;
+      add_usums(src);
       Op ea[TM], eb[TN];
       if constexpr (kOnce) {
 #pragma unroll
@@ -1013,6 +1051,13 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   // ------------------------------------------------------------------ epilogue
   // Element e of lane l in a 32x32 block is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32 of the block.
+  // biased int4: each row's and column's whole sum of u (lanes l and l + 32
+  // summed the two halves of every K-step)
+  int usum_tot_a[TM], usum_tot_b[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) usum_tot_a[i] = BIAS ? (int)usum_a[i] + __shfl_xor((int)usum_a[i], 32) : 0;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) usum_tot_b[j] = BIAS ? (int)usum_b[j] + __shfl_xor((int)usum_b[j], 32) : 0;
   // The value a lane stages for accumulator element e of block (i, j); the
   // dequant kind stages the raw sum and scales it when storing
   auto value = [&](int i, int j, int e) -> uint32_t {
@@ -1020,6 +1065,12 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       return __builtin_bit_cast(uint32_t, (float)acc[i][j][e]);
     } else if constexpr (E3M2) {
       return (uint32_t)(int32_t)acc[i][j][e];   // an integer below 2^24: exact
+    } else if constexpr (BIAS) {
+      // sum of (u_a - 8)(u_b - 8) over every k summed (nks stages of 2 ROWB
+      // values)
+      const int r = 8 * (e >> 2) + 4 * fh + (e & 3);   // row within block i
+      const int row_sum = __shfl(usum_tot_a[i], r);
+      return (uint32_t)(acc[i][j][e] - 8 * row_sum - 8 * (int)usum_tot_b[j] + 64 * 2 * ROWB * nks);
     } else if constexpr (KIND == KIND_I4 && !SX) {
       return (uint32_t)(acc[i][j][e] >> 8);   // undo the 16 x 16 scaling
     } else {

@@ -119,6 +119,10 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       return launch<256, 256>(
           (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads, false, kI4(2)>,
           args, 256, stream);
+    case CFG_128_S2_R256_BIAS:
+      return launch<128, 128>(
+          (const void*)&gemm_v3<KIND, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, kI4(4)>,
+          args, 256, stream);
     case CFG_256_S2_R128_W4:
       return launch<256, 256>(
           (const void*)&gemm_v3<KIND, 256, 256, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads, false, kI4(1)>,

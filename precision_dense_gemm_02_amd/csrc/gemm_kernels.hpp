@@ -2038,6 +2038,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_lds(GemmArgs p) {
 // compiler neither counts it nor places waits for it: the caller waits with
 // wait_vmcnt and then pins the destination with pin_after_wait before any
 // use (the data lands some time after the instruction issues).
+//
+// The invariant this relies on: between the load and its pin, the compiler
+// must not copy, spill or move `dst` (it believes the value is already
+// there, so a copy made before the data lands would read stale bits).  The
+// skinny kernels keep their in-flight fragments in fixed, unrolled slots
+// (no dynamic indexing), hold few registers (no pressure to split live
+// ranges), and the bit-exact GPU tests of the M <= 32 path and of the fused
+// W8A8 kernel fail if a toolchain ever breaks it.  The compiler-tracked load
+// builtin would be safe by construction, but the compiler does not count
+// the direct-to-LDS copies in between, so the wait it places before a
+// fragment's first use would also wait for the next round's loads.
 __device__ __forceinline__ void load_16_async(i32x4& dst, const i32x4& rsrc, uint32_t voff) {
   asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(voff), "s"(rsrc) : "memory");
 }

@@ -33,7 +33,8 @@ class OracleError(RuntimeError):
 
 _STATUS = {1: "integer result does not fit int32",
            2: "fp16 or fp64 operand is inf or NaN",
-           3: "bad row range, odd K or target bits outside [1, 53]"}
+           3: "bad row range, odd K or target bits outside [1, 53]",
+           4: "working buffer could not be allocated"}
 
 
 def build(force: bool = True) -> str:

@@ -58,7 +58,8 @@
  * Return value: 0 on success; 1 if an integer result does not fit int32
  * (the input is outside the library's contract); 2 if an fp16 or fp64
  * operand is inf or NaN (outside the contract); 3 for a bad row range or a
- * target bit count outside [1, 53].
+ * target bit count outside [1, 53]; 4 if a working buffer cannot be
+ * allocated.
  */
 #include <stdint.h>
 #include <math.h>
@@ -72,6 +73,7 @@
 #define ORACLE_INT32_RANGE 1
 #define ORACLE_NONFINITE 2
 #define ORACLE_BAD_RANGE 3
+#define ORACLE_NO_MEMORY 4
 
 static int bad_range(int64_t M, int64_t row_begin, int64_t row_end)
 {
@@ -298,8 +300,9 @@ int oracle_f64_emu(int64_t M, int64_t N, int64_t K, const double *A, const doubl
     if (!Bi || !eB) {
         free(Bi);
         free(eB);
-        return ORACLE_BAD_RANGE;
+        return ORACLE_NO_MEMORY;
     }
+    int no_memory = 0;
     for (int64_t j = 0; j < N; ++j) {
         eB[j] = row_exponent(B_t + j * K, K, &nonfinite);
         for (int64_t k = 0; k < K; ++k)
@@ -314,6 +317,11 @@ int oracle_f64_emu(int64_t M, int64_t N, int64_t K, const double *A, const doubl
             nonfinite = 1;
         }
         int64_t *Ai = (int64_t *)malloc((size_t)(K > 0 ? K : 1) * sizeof(int64_t));
+        if (!Ai) {
+#pragma omp atomic write
+            no_memory = 1;
+            continue;
+        }
         for (int64_t k = 0; k < K; ++k)
             Ai[k] = (int64_t)rint(ldexp(A[i * K + k], bits - eA));
         for (int64_t j = 0; j < N; ++j) {
@@ -327,6 +335,8 @@ int oracle_f64_emu(int64_t M, int64_t N, int64_t K, const double *A, const doubl
     }
     free(Bi);
     free(eB);
+    if (no_memory)
+        return ORACLE_NO_MEMORY;
     return nonfinite ? ORACLE_NONFINITE : ORACLE_OK;
 }
 

@@ -73,8 +73,31 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def split_kind(name: str) -> tuple:
+    """("i8", True) for "i8sk-...": a workload run through the split-K entry
+    point of its kind (with a workspace from splitk_workspace)."""
+    kind = name.split("-", 1)[0]
+    if kind in ("i8sk", "i4sk", "f16sk", "dqsk"):
+        return kind[:-2], True
+    return kind, False
+
+
 def parse_workload(name: str):
+    """(kind, M, N, K) of a workload name: "<kind>-<n>" for n^3 (the LLM and
+    W8A8 kinds: M = n), or "<kind>-<M>x<N>x<K>" for the i8, i4, f16 and dq
+    kinds and their split-K forms (i8sk, i4sk, f16sk, dqsk)."""
+    if name.count("-") != 1:
+        raise SystemExit(f"unknown workload {name}")
     kind, size = name.split("-")
+    base, _ = split_kind(name)
+    if "x" in size:
+        dims = size.split("x")
+        if base not in ("i8", "i4", "f16", "dq") or len(dims) != 3 or not all(d.isdigit() for d in dims):
+            raise SystemExit(f"unknown workload {name}")
+        M, N, K = (int(d) for d in dims)
+        return base, M, N, K
+    if not size.isdigit():
+        raise SystemExit(f"unknown workload {name}")
     size = int(size)
     if kind == "llm":
         from precision_dense_gemm_02_amd import inputs
@@ -82,9 +105,9 @@ def parse_workload(name: str):
     if kind in ("w8a8", "w8a8f"):
         from precision_dense_gemm_02_amd import inputs
         return ("w8" if kind == "w8a8" else "w8f"), size, inputs.LLM_N, inputs.LLM_K
-    if kind not in ("i8", "i4", "f16", "i4e", "i4g", "i8kn", "f64e"):
+    if base not in ("i8", "i4", "f16", "i4e", "i4g", "i8kn", "f64e"):
         raise SystemExit(f"unknown workload {name}")
-    return kind, size, size, size
+    return base, size, size, size
 
 
 class Workload:
@@ -100,11 +123,15 @@ class Workload:
         self.name = name
         self.kind, M, N, K = parse_workload(name)
         self.M, self.N, self.K = M, N, K
+        self.split = split_kind(name)[1]
         dev = torch.device("cuda:0")
 
         def to(x):
             return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
+        # split-K forms: the same inputs through the *_splitk entry point,
+        # with a workspace zeroed once here
+        ws_k = lp.splitk_workspace(M, N) if self.split else None
         kind = self.kind
         if kind == "i8":
             self.seed = inputs.seed_for("i8", M)
@@ -112,7 +139,10 @@ class Workload:
             self.host = p
             a, b = to(p.a), to(p.b_t)
             out = torch.empty((M, N), dtype=torch.int32, device=dev)
-            self.launch = lambda i: lp.gemm_i8(a, b, out=out)
+            if self.split:
+                self.launch = lambda i: lp.gemm_i8_splitk(a, b, ws_k, out=out)
+            else:
+                self.launch = lambda i: lp.gemm_i8(a, b, out=out)
             self.in_bytes = M * K + N * K
             self.out_bytes = 4 * M * N
         elif kind == "f64e":
@@ -150,7 +180,10 @@ class Workload:
             self.host = p
             a, b = to(p.a_packed), to(p.b_packed)
             out = torch.empty((M, N), dtype=torch.int32, device=dev)
-            self.launch = lambda i: lp.gemm_i4(a, b, K, out=out)
+            if self.split:
+                self.launch = lambda i: lp.gemm_i4_splitk(a, b, ws_k, K, out=out)
+            else:
+                self.launch = lambda i: lp.gemm_i4(a, b, K, out=out)
             self.in_bytes = (M * K + N * K) // 2
             self.out_bytes = 4 * M * N
         elif kind in ("i4e", "i4g"):
@@ -182,7 +215,10 @@ class Workload:
             self.host = p
             a, b = to(p.a), to(p.b_t)
             out = torch.empty((M, N), dtype=torch.float32, device=dev)
-            self.launch = lambda i: lp.gemm_f16(a, b, out=out)
+            if self.split:
+                self.launch = lambda i: lp.gemm_f16_splitk(a, b, ws_k, out=out)
+            else:
+                self.launch = lambda i: lp.gemm_f16(a, b, out=out)
             self.in_bytes = 2 * (M * K + N * K)
             self.out_bytes = 4 * M * N
         elif kind == "w8f":
@@ -216,16 +252,22 @@ class Workload:
             self.launch = step
             self.in_bytes = 2 * M * K + N * K + 4 * N
             self.out_bytes = 4 * M * N
-        else:  # dequantised LLM projection
+        else:  # dequantised LLM projection (or a dequantised product of any shape)
             self.seed = inputs.seed_for("llm", M)
-            p = inputs.llm_problem(M, self.seed)
+            if name.startswith("llm-"):
+                p = inputs.llm_problem(M, self.seed)
+            else:
+                p = inputs.int8_problem(M, N, K, self.seed, scales=True)
             self.host = p
             a, rs, cs = to(p.a), to(p.row_scale), to(p.col_scale)
             # rotate weight copies so that the timed launches stream B from HBM
             copies = max(1, -(-336 * 2 ** 20 // (N * K)))
             bs = [to(p.b_t)] + [to(p.b_t) for _ in range(copies - 1)]
             out = torch.empty((M, N), dtype=torch.float32, device=dev)
-            self.launch = lambda i: lp.gemm_i8_dequant(a, bs[i % len(bs)], rs, cs, out=out)
+            if self.split:
+                self.launch = lambda i: lp.gemm_i8_dequant_splitk(a, bs[i % len(bs)], rs, cs, ws_k, out=out)
+            else:
+                self.launch = lambda i: lp.gemm_i8_dequant(a, bs[i % len(bs)], rs, cs, out=out)
             self.in_bytes = M * K + N * K + 4 * (M + N)
             self.out_bytes = 4 * M * N
         self.out = out
@@ -507,9 +549,9 @@ def platform_library(steps: int, warmup: int, settle_s: float, n: int = 8192) ->
 # the kernel each square workload runs at 8192 (the persistent configuration
 # 47 for int8 and fp16, configuration 0 for int4)
 TRAFFIC_KERNELS = {
-    "i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false>(lpgemm::GemmArgs)",
-    "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false, false, 0, false>(lpgemm::GemmArgs)",
-    "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false>(lpgemm::GemmArgs)"}
+    "i8-8192": "void lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false, false>(lpgemm::GemmArgs)",
+    "i4-8192": "void lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false, false, 0, false, false>(lpgemm::GemmArgs)",
+    "f16-8192": "void lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false, false>(lpgemm::GemmArgs)"}
 
 
 def _median_counter(path: str, kernel: str, counter: str) -> float:

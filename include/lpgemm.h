@@ -28,7 +28,9 @@
  *
  * Ownership: every pointer is device memory owned by the caller, which must
  * keep it valid until the enqueued work completes.  The library allocates no
- * memory, keeps no per-call state and may be called from several host threads.
+ * memory, keeps no per-call state and may be called from several host threads
+ * (the split-K entry points keep per-tile counters in the caller's
+ * workspace).
  * C must not overlap A, B or the scales.
  *
  * Degenerate sizes: M = 0 or N = 0 is an empty product; the call returns
@@ -185,6 +187,50 @@ lpgemm_status lpgemm_f16(int64_t M, int64_t N, int64_t K, const void *A, const v
 lpgemm_status lpgemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A,
                                 const int8_t *B, const float *row_scale,
                                 const float *col_scale, float *C, hipStream_t stream);
+
+/* Split-K variants of lpgemm_i8, lpgemm_i4, lpgemm_f16 and lpgemm_i8_dequant
+ * for products with few output tiles and a long K, whose tiles alone would
+ * leave most of the GPU idle (the PTX-vs-WMMA summary page's INT4 paragraph
+ * picks the pipeline per problem size).  Same operation, arguments,
+ * layouts, result and errors as the entry point without the suffix, plus a
+ * caller-provided workspace in device memory:
+ *   lpgemm_splitk_workspace(M, N) is the number of bytes the automatic
+ *   choice may use for an M x N product on the current device, whatever K
+ *   is (0 when that product never splits; -1 for sizes outside 0..2^31-1
+ *   or when the device cannot be queried).
+ * The automatic choice splits when M > 64, the product's 128 x 128 output
+ * tiles number at most a quarter of the GPU's compute units, and each
+ * operand row holds more than 31 x 256 bytes (int8 K >= 7952, fp16
+ * K >= 3976, int4 K >= 15904).  The K dimension of each tile is then split
+ * over 4 workgroups; each writes its partial sums to the workspace and the
+ * last of a tile to finish adds them and writes C.
+ * The integer results are exact and equal to the unsplit entry point's bit
+ * for bit; the fp16 result adds the parts in a fixed order, so it is
+ * deterministic and within the same error bound, but may differ from the
+ * unsplit one in the last bits.  Any other shape, a null workspace, or one
+ * smaller than lpgemm_splitk_workspace(M, N), runs the product unsplit.
+ * The workspace must be 256-byte aligned and ZEROED ONCE before its first
+ * use (for instance with hipMemset): its first 4 KiB hold one arrival
+ * counter per tile, and every call leaves the counters at zero when it
+ * completes, so the same workspace serves any number of later calls, of any
+ * shape, without clearing (a product of more than 1024 tiles never
+ * splits).  Calls that
+ * share a workspace must not overlap in time (serialise them, for instance
+ * on one stream).  Errors, after the unsuffixed entry point's argument
+ * checks: INVALID_VALUE for workspace_bytes < 0, MISALIGNED for a workspace
+ * that is not 256-byte aligned.  The workspace must not overlap A, B, C or
+ * the scales. */
+int64_t lpgemm_splitk_workspace(int64_t M, int64_t N);
+lpgemm_status lpgemm_i8_splitk(int64_t M, int64_t N, int64_t K, const int8_t *A, const int8_t *B,
+                               int32_t *C, void *workspace, int64_t workspace_bytes, hipStream_t stream);
+lpgemm_status lpgemm_i4_splitk(int64_t M, int64_t N, int64_t K, const uint8_t *A_packed,
+                               const uint8_t *B_packed, int32_t *C, void *workspace,
+                               int64_t workspace_bytes, hipStream_t stream);
+lpgemm_status lpgemm_f16_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B, float *C,
+                                void *workspace, int64_t workspace_bytes, hipStream_t stream);
+lpgemm_status lpgemm_i8_dequant_splitk(int64_t M, int64_t N, int64_t K, const int8_t *A, const int8_t *B,
+                                       const float *row_scale, const float *col_scale, float *C,
+                                       void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /* Largest M of lpgemm_w8a8_fused: one band of 32 rows, the decode-sized
  * products it is meant for. */

@@ -81,6 +81,14 @@ def load_library():
         lib.lpgemm_status_string.restype = ctypes.c_char_p
         lib.lpgemm_version.argtypes = []
         lib.lpgemm_version.restype = ctypes.c_int
+        for name in ("lpgemm_i8_splitk", "lpgemm_i4_splitk", "lpgemm_f16_splitk"):
+            f = getattr(lib, name)
+            f.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i64, _p]
+            f.restype = ctypes.c_int
+        lib.lpgemm_i8_dequant_splitk.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _p]
+        lib.lpgemm_i8_dequant_splitk.restype = ctypes.c_int
+        lib.lpgemm_splitk_workspace.argtypes = [_i64, _i64]
+        lib.lpgemm_splitk_workspace.restype = _i64
         lib.lpgemm_config_count.argtypes = []
         lib.lpgemm_config_count.restype = ctypes.c_int
         lib.lpgemm_force_config.argtypes = [ctypes.c_int]
@@ -260,6 +268,118 @@ def gemm_i8_dequant(a, b_t, row_scale, col_scale, out=None):
                                                 row_scale.data_ptr(), col_scale.data_ptr(),
                                                 out.data_ptr(), _stream_handle(dev)),
                "lpgemm_i8_dequant")
+    return out
+
+
+def splitk_workspace_bytes(M: int, N: int) -> int:
+    """Workspace bytes the split-K entry points use for an M x N product on
+    the current device (0: the product runs unsplit)."""
+    n = int(load_library().lpgemm_splitk_workspace(M, N))
+    if n < 0:
+        raise ValueError(f"lpgemm_splitk_workspace({M}, {N}) failed")
+    return n
+
+
+def splitk_workspace(M: int, N: int, device=None):
+    """A zeroed uint8 GPU tensor for the split-K entry points on an M x N
+    product (at least 256 bytes).  Zeroed once here; every call leaves it
+    reusable, so keep it for later calls of the same or smaller size."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        n = splitk_workspace_bytes(M, N)
+    return torch.zeros((max(n, 256),), dtype=torch.uint8, device=dev)
+
+
+def _workspace(ws, dev):
+    torch = _torch()
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or not ws.is_cuda \
+            or not ws.is_contiguous() or ws.device != dev:
+        raise ValueError("workspace must be a contiguous uint8 tensor on the operands' GPU")
+    return ws.data_ptr(), ws.numel()
+
+
+def gemm_i8_splitk(a, b_t, workspace, out=None):
+    """gemm_i8 with K split over workgroups for products with few 128 x 128
+    tiles; `workspace` from splitk_workspace (zeroed once, reusable)."""
+    torch = _torch()
+    _operand(a, torch.int8, "a")
+    _operand(b_t, torch.int8, "b_t")
+    if a.shape[1] != b_t.shape[1]:
+        raise ValueError(f"K mismatch: a {tuple(a.shape)}, b_t {tuple(b_t.shape)}")
+    dev = _same_device(a, b_t)
+    M, K = a.shape
+    N = b_t.shape[0]
+    wp, wn = _workspace(workspace, dev)
+    out = _output(out, (M, N), torch.int32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_i8_splitk(M, N, K, a.data_ptr(), b_t.data_ptr(), out.data_ptr(), wp, wn,
+                                               _stream_handle(dev)), "lpgemm_i8_splitk")
+    return out
+
+
+def gemm_i4_splitk(a_packed, b_packed, workspace, K: Optional[int] = None, out=None):
+    """gemm_i4 with K split over workgroups (see gemm_i8_splitk)."""
+    torch = _torch()
+    _operand(a_packed, torch.uint8, "a_packed")
+    _operand(b_packed, torch.uint8, "b_packed")
+    if a_packed.shape[1] != b_packed.shape[1]:
+        raise ValueError("packed K mismatch")
+    if K is None:
+        K = 2 * a_packed.shape[1]
+    if 2 * a_packed.shape[1] != K:
+        raise ValueError(f"K={K} does not match packed width {a_packed.shape[1]}")
+    dev = _same_device(a_packed, b_packed)
+    M = a_packed.shape[0]
+    N = b_packed.shape[0]
+    wp, wn = _workspace(workspace, dev)
+    out = _output(out, (M, N), torch.int32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_i4_splitk(M, N, K, a_packed.data_ptr(), b_packed.data_ptr(),
+                                               out.data_ptr(), wp, wn, _stream_handle(dev)), "lpgemm_i4_splitk")
+    return out
+
+
+def gemm_f16_splitk(a, b_t, workspace, out=None):
+    """gemm_f16 with K split over workgroups (see gemm_i8_splitk); the parts
+    are added in a fixed order."""
+    torch = _torch()
+    _operand(a, torch.float16, "a")
+    _operand(b_t, torch.float16, "b_t")
+    if a.shape[1] != b_t.shape[1]:
+        raise ValueError(f"K mismatch: a {tuple(a.shape)}, b_t {tuple(b_t.shape)}")
+    dev = _same_device(a, b_t)
+    M, K = a.shape
+    N = b_t.shape[0]
+    wp, wn = _workspace(workspace, dev)
+    out = _output(out, (M, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_f16_splitk(M, N, K, a.data_ptr(), b_t.data_ptr(), out.data_ptr(), wp, wn,
+                                                _stream_handle(dev)), "lpgemm_f16_splitk")
+    return out
+
+
+def gemm_i8_dequant_splitk(a, b_t, row_scale, col_scale, workspace, out=None):
+    """gemm_i8_dequant with K split over workgroups (see gemm_i8_splitk)."""
+    torch = _torch()
+    _operand(a, torch.int8, "a")
+    _operand(b_t, torch.int8, "b_t")
+    if a.shape[1] != b_t.shape[1]:
+        raise ValueError(f"K mismatch: a {tuple(a.shape)}, b_t {tuple(b_t.shape)}")
+    M, K = a.shape
+    N = b_t.shape[0]
+    for t, n, name in ((row_scale, M, "row_scale"), (col_scale, N, "col_scale")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 1 \
+                or t.shape[0] != n or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 GPU vector of length {n}")
+    dev = _same_device(a, b_t, row_scale, col_scale)
+    wp, wn = _workspace(workspace, dev)
+    out = _output(out, (M, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().lpgemm_i8_dequant_splitk(M, N, K, a.data_ptr(), b_t.data_ptr(),
+                                                       row_scale.data_ptr(), col_scale.data_ptr(),
+                                                       out.data_ptr(), wp, wn, _stream_handle(dev)),
+               "lpgemm_i8_dequant_splitk")
     return out
 
 

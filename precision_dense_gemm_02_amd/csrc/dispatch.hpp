@@ -135,7 +135,8 @@ enum KernelCfg {
   CFG_STREAM_64x64 = 57,         // ... 64 x 64 tiles, A 3 stages, B 14 stages
   CFG_256_S2_R128_EARLY = 58,    // configuration 0 with half of each stage's loads issued one K-step earlier
   CFG_128_S2_R256_BIAS = 59,     // configuration 36, int4 expanded biased (u = v + 8) with sum corrections
-  CFG_COUNT = 60
+  CFG_128_S2_R256_SPLITK = 60,   // configuration 36 (int4: 48) with K split over workgroups (needs a workspace)
+  CFG_COUNT = 61
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -146,7 +147,7 @@ inline int stage_row_bytes(KernelCfg c) {
           c == CFG_256_S5_R64_NT || c == CFG_256_S4_R64_NT)
              ? 64
              : ((c == CFG_128x64_S3_R256 || c == CFG_128_S2_R256 || c == CFG_128_S2_R256_W4 ||
-                 c == CFG_128_S2_R256_SX || c == CFG_128_S2_R256_BIAS)
+                 c == CFG_128_S2_R256_SX || c == CFG_128_S2_R256_BIAS || c == CFG_128_S2_R256_SPLITK)
                     ? 256
                     : 128);
 }
@@ -202,6 +203,70 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   return CFG_V1_64x64;
 }
 
+// Split-K over 128 x 128 tiles (configuration 60) for products with few
+// tiles and a long K: each tile's K-stages are split over up to four
+// workgroups, which write raw partial sums to a caller-provided workspace;
+// the last one of a tile to finish adds them and runs the epilogue, so the
+// result is the unsplit kernel's bit for bit for the integer kinds.  The
+// hand-over (the parts written through to the device's coherence point, an
+// arrival counter, the parts read back) costs a few microseconds per tile,
+// so the automatic choice splits only products whose 128 x 128 tiles fill
+// at most a quarter of the CUs, four ways, and only when K spans at least
+// 32 K-stages of 256 bytes (8 per part).  Measured (graph replay, one
+// MI355X): int8 512 x 2048 x 32768 2.5 times, 256 x 4096 x 16384 2.0 times,
+// 1024 x 1024 x 8192 1.5 times, 300 x 520 x 8208 1.2 times as fast; fp16
+// 1024 x 1024 x 8192 1.9 times; int4 1024 x 1024 x 16384 2.3 times.  Two
+// parts of 8 stages lost: int8 1024 x 1024 x 4096 16.4 against 12.8 us,
+// the LLM projection at M = 128, K = 4096 (112 tiles) 23 against 18 us.
+//
+// Workspace layout, the same for every shape so that one workspace serves
+// products of any size in turn: 4 KiB of 32-bit arrival counters (tile t
+// uses counter t; all are zero between calls), then tiles x splits slots of
+// 128 x 128 32-bit partial sums.  Products of more than 1024 tiles do not
+// split.
+constexpr int64_t kSplitTile = 128;
+constexpr int64_t kSplitSlotBytes = kSplitTile * kSplitTile * 4;
+constexpr int kMaxSplits = 4;
+constexpr int kMinStagesPerSplit = 8;
+constexpr int64_t kSplitCounterBytes = 4096;
+constexpr int64_t kMaxSplitTiles = kSplitCounterBytes / 4;
+
+inline int64_t splitk_bytes(int64_t ntiles, int splits) {
+  return splits > 1 ? kSplitCounterBytes + ntiles * splits * kSplitSlotBytes : 0;
+}
+
+// Whether the automatic choice splits an M x N product on `cu_count` CUs
+// at all (any K): above 64 rows (below that the skinny kernels split K
+// inside a workgroup) and when the 128 x 128 tiles fill at most a quarter
+// of the CUs.  Such a product may use up to kMaxSplits parts.
+inline bool splitk_auto_shape(int64_t M, int64_t N, int cu_count) {
+  return M > 64 && (int64_t)tiles(M, kSplitTile) * tiles(N, kSplitTile) <= cu_count / 4;
+}
+
+// Parts for the automatic choice with `nks` 256-byte K-stages (1: no split).
+inline int splitk_auto_splits(int64_t M, int64_t N, int nks, int cu_count) {
+  if (!splitk_auto_shape(M, N, cu_count)) return 1;
+  return nks >= kMaxSplits * kMinStagesPerSplit ? kMaxSplits : 1;
+}
+
+// Parts for a launch of configuration 60 with `nks` K-stages and a
+// workspace of `ws_bytes`: the automatic count (when forced: at least 2,
+// at most one part per K-stage and as many as fill the CUs once), and 1 when
+// the workspace is missing or too small.
+inline int splitk_launch_splits(int64_t M, int64_t N, int nks, int cu_count, const void* ws, int64_t ws_bytes) {
+  if (!ws) return 1;
+  const int64_t t = (int64_t)tiles(M, kSplitTile) * tiles(N, kSplitTile);
+  if (t > kMaxSplitTiles) return 1;
+  int s = splitk_auto_splits(M, N, nks, cu_count);
+  if (s < 2) {
+    const int64_t fill = cu_count / t;
+    s = fill > kMaxSplits ? kMaxSplits : (fill < 2 ? 2 : (int)fill);
+  }
+  if (s > nks) s = nks;
+  if (s < 2 || ws_bytes < splitk_bytes(t, s)) return 1;
+  return s;
+}
+
 // B stored K x N row-major runs on the LDS-pipelined kernels with 128-byte
 // stage rows: 128 k-rows of B per stage.
 inline bool supports_kxn(int c) {
@@ -244,26 +309,46 @@ lpgemm_status launch_persistent(const void* fn, GemmArgs args, int threads, hipS
   return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
 }
 
+// A split-K launch: a grid of tiles x splits workgroups (gemm_v3<..., SPK =
+// true>), with the workspace's counters and slots in the arguments.
+template <int BM, int BN>
+lpgemm_status launch_split(const void* fn, GemmArgs args, int threads, hipStream_t stream, int splits, void* ws) {
+  args.tiles_m = tiles(args.M, BM);
+  args.tiles_n = tiles(args.N, BN);
+  args.group_m = 8;
+  const int64_t nblocks = (int64_t)args.tiles_m * args.tiles_n;
+  if (nblocks > INT32_MAX) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  args.splits = splits;
+  args.split_count = static_cast<uint32_t*>(ws);
+  args.split_part = splits > 1 ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kSplitCounterBytes) : nullptr;
+  void* kargs[] = {&args};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks, (unsigned)splits), dim3(threads), kargs, 0, stream);
+  return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
+}
+
 // One GEMM of the given kind (BKN: B stored K x N) on `stream`: validation,
-// the configuration for the shape, and the kernel launch.  Defined in
-// run_kernels.hpp; instantiated in run_*.hip.
+// the configuration for the shape, and the kernel launch.  `ws` (may be
+// null) is a split-K workspace of `ws_bytes`; with one, short products may
+// run split (configuration 60).  Defined in run_kernels.hpp; instantiated in
+// run_*.hip.
 template <int KIND, bool BKN = false>
 lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, const float* rs,
-                  const float* cs, hipStream_t stream, int modulus = 0);
+                  const float* cs, hipStream_t stream, int modulus = 0, void* ws = nullptr,
+                  int64_t ws_bytes = 0);
 
 extern template lpgemm_status run<KIND_I8, false>(int64_t, int64_t, int64_t, const void*, const void*, void*,
-                                                  const float*, const float*, hipStream_t, int);
+                                                  const float*, const float*, hipStream_t, int, void*, int64_t);
 extern template lpgemm_status run<KIND_I4, false>(int64_t, int64_t, int64_t, const void*, const void*, void*,
-                                                  const float*, const float*, hipStream_t, int);
+                                                  const float*, const float*, hipStream_t, int, void*, int64_t);
 extern template lpgemm_status run<KIND_F16, false>(int64_t, int64_t, int64_t, const void*, const void*, void*,
-                                                   const float*, const float*, hipStream_t, int);
+                                                   const float*, const float*, hipStream_t, int, void*, int64_t);
 extern template lpgemm_status run<KIND_I8_DEQUANT, false>(int64_t, int64_t, int64_t, const void*, const void*,
-                                                          void*, const float*, const float*, hipStream_t, int);
+                                                          void*, const float*, const float*, hipStream_t, int, void*, int64_t);
 extern template lpgemm_status run<KIND_I4_E3M2, false>(int64_t, int64_t, int64_t, const void*, const void*,
-                                                       void*, const float*, const float*, hipStream_t, int);
+                                                       void*, const float*, const float*, hipStream_t, int, void*, int64_t);
 extern template lpgemm_status run<KIND_I8_MOD, false>(int64_t, int64_t, int64_t, const void*, const void*,
-                                                      void*, const float*, const float*, hipStream_t, int);
+                                                      void*, const float*, const float*, hipStream_t, int, void*, int64_t);
 extern template lpgemm_status run<KIND_I8, true>(int64_t, int64_t, int64_t, const void*, const void*, void*,
-                                                 const float*, const float*, hipStream_t, int);
+                                                 const float*, const float*, hipStream_t, int, void*, int64_t);
 
 }  // namespace lpgemm

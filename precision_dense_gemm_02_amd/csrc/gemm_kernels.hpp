@@ -65,6 +65,12 @@ struct GemmArgs {
   int group_m;          // tile rows per raster group
   int modulus;          // KIND_I8_MOD: C[i][j] = (A.B)[i][j] mod modulus (0 < modulus <= 256), uint8
   double inv_modulus;   // KIND_I8_MOD: RN(1 / modulus)
+  // split-K (gemm_v3<..., SPK = true>): K-stages split `splits` ways over
+  // gridDim.y; per tile one arrival counter (zero between launches) and
+  // `splits` slots of raw 32-bit partial accumulators
+  int splits;
+  uint32_t* split_count;
+  uint32_t* split_part;
 };
 
 // Position of 16-byte chunk `c` of LDS row `r` within that row.  XOR with a
@@ -477,6 +483,25 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)p);
 }
 
+// Four accumulator elements summed over split-K slots: int32 adds (exact,
+// wrapping like the MFMA's own accumulation) or binary32 adds in the order
+// the slots are given.
+template <typename AccT>
+struct Acc_elem4 {
+  using E = typename std::conditional<std::is_same<AccT, f32x16>::value, float, int>::type;
+  E v[4];
+  __device__ __forceinline__ void add(i32x4 x, bool first) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int xk = x[k];   // a vector element is not an object: copy it first
+      const E e = __builtin_bit_cast(E, xk);
+      if constexpr (std::is_same<E, float>::value) v[k] = first ? e : v[k] + e;
+      else v[k] = first ? e : (E)((uint32_t)v[k] + (uint32_t)e);
+    }
+  }
+  __device__ __forceinline__ E get(int k) const { return v[k]; }
+};
+
 // ---------------------------------------------------------------------------
 // Four-wave kernel with direct-to-LDS loads and an LDS-staged epilogue.
 //
@@ -599,9 +624,21 @@ struct RowLayout<64> {
 // staged and stored, and the next tile's first fragments are read before
 // the epilogue.  The epilogue therefore stages 32 rows per wave at a time
 // and keeps clear of the LDS stage those loads fill.  Two stages only.
+//
+// SPK: split-K.  Workgroup (x, y) of a grid of tiles x p.splits sums the
+// y-th of p.splits contiguous runs of the tile's K-stages.  Every workgroup
+// writes its raw accumulators to its own slot of p.split_part (each lane its
+// registers, in register order, so no layout is involved), publishes them
+// with a device-scope release and counts itself in at the tile's counter;
+// the one that arrives last (an acquire, no waiting) resets the counter to
+// zero for the next launch, adds the slots in split order (fp16: a fixed
+// order, so the result does not depend on which workgroup came last) and
+// runs the epilogue on the sum.  Nothing waits for another workgroup, so no
+// workgroup can be held up by one that is not resident.  p.splits = 1 is
+// the plain kernel.
 template <int KIND, int BM, int BN, int STAGES, int ROWB, int CPOL = 0, bool SPLIT = false,
           bool BKN = false, int LSTEPS = 0, bool NTC = false, int BSPLIT = 0, bool PF = false,
-          bool HIL = false, bool PERSIST = false, int I4MODE = 0, bool EARLY = false>
+          bool HIL = false, bool PERSIST = false, int I4MODE = 0, bool EARLY = false, bool SPK = false>
 __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   using Layout = RowLayout<ROWB>;
@@ -647,6 +684,8 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   constexpr int kEpiWave = kEpiRows * kEpiPitch;
   constexpr int kEpiLds = 4 * kEpiWave;
   static_assert(!PERSIST || (STAGES == 2 && !PF && !BKN && !SPLIT && KIND != KIND_I8_MOD), "persistent variant");
+  static_assert(!SPK || (!PERSIST && !BIAS && !BKN && !PF && KIND != KIND_I8_MOD && KIND != KIND_I4_E3M2),
+                "split-K variant");
   // persistent: the epilogue avoids the stage the next tile's first loads
   // fill.  Stage 0 in flight: the four waves stage in [kStage, kStage +
   // kEpiLds).  Stage 1 in flight: waves 0-2 stage in stage 0's space, wave 3
@@ -675,6 +714,11 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   if constexpr (PERSIST) tile_of(p, logical, tm, tn);
   else tile_coords(p, tm, tn);
   int m0 = tm * BM, n0 = tn * BN;
+  // split-K: this workgroup's run of K-stages [kb, kb + nks)
+  const int split = SPK ? (int)blockIdx.y : 0;
+  const int kb = SPK ? (int)(((int64_t)split * p.k_stages) / p.splits) : 0;
+  const int nks = SPK ? (int)(((int64_t)(split + 1) * p.k_stages) / p.splits) - kb
+                      : p.k_stages;   // 0 when K = 0: C is written as zeros
   // buffer resources over a tile's A and B row panels
   auto panel_a = [&](int mm0) -> i32x4 {
     return make_rsrc(p.A + (size_t)mm0 * p.row_bytes, min(BM, p.M - mm0) * p.row_bytes);
@@ -751,7 +795,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   // stage s of this tile (persistent: s = nks is the next tile's stage 0)
   auto issue_load = [&](int t, int s) {
     const bool next = PERSIST && s >= p.k_stages;
-    const uint32_t kbyte = next ? 0u : (uint32_t)s * ROWB;
+    const uint32_t kbyte = next ? 0u : (uint32_t)(kb + s) * ROWB;
     const int g = group_of(t);
     uint32_t off;
     if (BKN && !is_a(t)) {
@@ -953,7 +997,6 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     }
   };
 
-  const int nks = p.k_stages;   // 0 when K = 0: C is written as zeros
   // the prefetch of stage s + STAGES is issued in this K-step of stage s,
   // after the stage's own loads
   constexpr int kPfStep = kLoadSteps < KSTEPS - 1 ? kLoadSteps : KSTEPS - 1;
@@ -1086,6 +1129,94 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   // stage 0, which the fragment reads of its first K-step are reading.
   wait_vmcnt<0>();
   wait_lgkmcnt0();
+  if constexpr (SPK) {
+    if (p.splits > 1) {
+      // The tile's slots, split sp at sp * kSlotBytes: 4 waves x TM*TN
+      // blocks x 4 quads x 64 lanes of 16 bytes; a lane's quad q of block b
+      // is its accumulator elements 4q .. 4q + 3.
+      //
+      // Publishing without cache flushes: the slots are written and read
+      // with device-scope (sc1) accesses, the form device-scope relaxed
+      // atomics take on this chip, which write through to the device's
+      // coherence point and read from it.  A workgroup waits until its
+      // stores are acknowledged (vmcnt 0) before it counts itself in with a
+      // device-scope atomic, and the last arrival reads the slots only after
+      // that atomic has returned, so every slot it reads is complete.  (A
+      // device-scope release/acquire pair would write back and invalidate
+      // the whole L2 around each arrival, which costs far more than the
+      // split saves.)
+      constexpr int kSlotBytes = 4 * TM * TN * 16 * 64 * 4;
+      constexpr int kSc1 = 16;   // cache-policy bits: device scope
+      const int tile = (int)blockIdx.x;
+      const __amdgpu_buffer_rsrc_t slots = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.split_part + (size_t)tile * p.splits * (kSlotBytes / 4)), 0, p.splits * kSlotBytes,
+          kBufferWord3);
+      auto slot_off = [&](int sp, int i, int j, int q) -> int {
+        return sp * kSlotBytes + (((wave * TM + i) * TN + j) * 4 + q) * 1024 + lane * 16;
+      };
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            i32x4 v;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              // (a vector element is not an object: copy it before the bit cast)
+              const auto e = acc[i][j][4 * q + x];
+              v[x] = __builtin_bit_cast(int, e);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(v, slots, slot_off(split, i, j, q), 0, kSc1);
+          }
+      __shared__ uint32_t arrived;
+      wait_vmcnt<0>();   // this wave's slot stores acknowledged
+      block_barrier();   // ... every wave's
+      if (tid == 0) arrived = __hip_atomic_fetch_add(p.split_count + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_lgkmcnt0();
+      block_barrier();
+      if (arrived != (uint32_t)(p.splits - 1)) return;
+      // the last arrival: the counter back to zero for the next launch, then
+      // the sum in split order, this workgroup's own part from its registers
+      if (tid == 0) __hip_atomic_store(p.split_count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // one batch of loads per other split (a single wait for each), added
+      // into the running sum in split order
+      Acc_elem4<Acc> sum[TM][TN][4];
+      for (int sp = 0; sp < p.splits; ++sp) {
+        i32x4 part[TM][TN][4];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (sp == split) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                  const auto e = acc[i][j][4 * q + x];
+                  part[i][j][q][x] = __builtin_bit_cast(int, e);
+                }
+              } else {
+                part[i][j][q] = __builtin_amdgcn_raw_buffer_load_b128(slots, slot_off(sp, i, j, q), 0, kSc1);
+              }
+            }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sum[i][j][q].add(part[i][j][q], sp == 0);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[i][j][4 * q + x] = sum[i][j][q].get(x);
+    }
+  }
   if constexpr (KIND != KIND_I8_MOD) {
     // Every kind but the reduced one goes through LDS: each wave transposes
     // kEpiRows rows of its quadrant at a time so that a lane holds 4

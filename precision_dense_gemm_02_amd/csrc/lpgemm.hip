@@ -4,7 +4,9 @@
 // checks once per device that the device is gfx950, picks a tile
 // configuration for the shape, and enqueues one kernel on the caller's
 // stream.  Nothing is allocated and no state is kept between calls apart from
-// the per-device property cache (and the configuration an ablation pins).
+// the per-device property cache (and the configuration an ablation pins);
+// the split-K entry points keep their per-tile counters in the caller's
+// workspace.
 // The GEMM launches themselves are in run_*.hip (one translation unit per
 // operand kind, see dispatch.hpp).
 #include <hip/hip_runtime.h>
@@ -386,6 +388,35 @@ lpgemm_status lpgemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t* A
   return run<KIND_I8_DEQUANT>(M, N, K, A, B, C, row_scale, col_scale, stream);
 }
 
+int64_t lpgemm_splitk_workspace(int64_t M, int64_t N) {
+  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX) return -1;
+  DeviceInfo dev;
+  if (current_device(dev) != LPGEMM_SUCCESS) return -1;
+  const int64_t t = (int64_t)tiles(M, kSplitTile) * tiles(N, kSplitTile);
+  return splitk_auto_shape(M, N, dev.cu_count) ? splitk_bytes(t, kMaxSplits) : 0;
+}
+
+lpgemm_status lpgemm_i8_splitk(int64_t M, int64_t N, int64_t K, const int8_t* A, const int8_t* B, int32_t* C,
+                               void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return run<KIND_I8>(M, N, K, A, B, C, nullptr, nullptr, stream, 0, workspace, workspace_bytes);
+}
+
+lpgemm_status lpgemm_i4_splitk(int64_t M, int64_t N, int64_t K, const uint8_t* A_packed, const uint8_t* B_packed,
+                               int32_t* C, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return run<KIND_I4>(M, N, K, A_packed, B_packed, C, nullptr, nullptr, stream, 0, workspace, workspace_bytes);
+}
+
+lpgemm_status lpgemm_f16_splitk(int64_t M, int64_t N, int64_t K, const void* A, const void* B, float* C,
+                                void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return run<KIND_F16>(M, N, K, A, B, C, nullptr, nullptr, stream, 0, workspace, workspace_bytes);
+}
+
+lpgemm_status lpgemm_i8_dequant_splitk(int64_t M, int64_t N, int64_t K, const int8_t* A, const int8_t* B,
+                                       const float* row_scale, const float* col_scale, float* C, void* workspace,
+                                       int64_t workspace_bytes, hipStream_t stream) {
+  return run<KIND_I8_DEQUANT>(M, N, K, A, B, C, row_scale, col_scale, stream, 0, workspace, workspace_bytes);
+}
+
 lpgemm_status lpgemm_w8a8_fused(int64_t M, int64_t N, int64_t K, const void* X, const int8_t* W,
                                 const float* w_scale, float* C, hipStream_t stream) {
   // the dequantising product's checks, with w_scale in both scale slots (the
@@ -467,7 +498,7 @@ const char* lpgemm_status_string(lpgemm_status status) {
   return "unknown status";
 }
 
-int lpgemm_version(void) { return 200; }
+int lpgemm_version(void) { return 300; }
 
 int lpgemm_config_count(void) { return CFG_COUNT; }
 

@@ -5,9 +5,9 @@
 
 namespace lpgemm {
 template lpgemm_status run<KIND_I4_E3M2, false>(int64_t, int64_t, int64_t, const void*, const void*, void*,
-                                                const float*, const float*, hipStream_t, int);
+                                                const float*, const float*, hipStream_t, int, void*, int64_t);
 template lpgemm_status run<KIND_I8_MOD, false>(int64_t, int64_t, int64_t, const void*, const void*, void*,
-                                               const float*, const float*, hipStream_t, int);
+                                               const float*, const float*, hipStream_t, int, void*, int64_t);
 template lpgemm_status run<KIND_I8, true>(int64_t, int64_t, int64_t, const void*, const void*, void*,
-                                          const float*, const float*, hipStream_t, int);
+                                          const float*, const float*, hipStream_t, int, void*, int64_t);
 }  // namespace lpgemm

@@ -3,5 +3,5 @@
 
 namespace lpgemm {
 template lpgemm_status run<KIND_I4, false>(int64_t, int64_t, int64_t, const void*, const void*, void*, const float*,
-                                       const float*, hipStream_t, int);
+                                       const float*, hipStream_t, int, void*, int64_t);
 }  // namespace lpgemm

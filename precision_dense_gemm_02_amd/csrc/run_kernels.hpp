@@ -9,7 +9,8 @@ namespace lpgemm {
 
 template <int KIND, bool BKN>
 lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
-                  const float* rs, const float* cs, hipStream_t stream, int modulus) {
+                  const float* rs, const float* cs, hipStream_t stream, int modulus, void* ws,
+                  int64_t ws_bytes) {
   // K x N B: k-rows of N bytes must start 16-byte aligned and the matrix
   // must fit the 32-bit offsets of its buffer resource (a shape error, so it
   // ranks with the K checks: after negative sizes, before pointers)
@@ -19,6 +20,9 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   bool nothing_to_do = false;
   lpgemm_status st = validate((Kind)KIND, M, N, K, A, B, C, rs, cs, nothing_to_do);
   if (st != LPGEMM_SUCCESS || nothing_to_do) return st;
+  // split-K workspace (the *_splitk entry points): may be null
+  if (ws_bytes < 0) return LPGEMM_ERROR_INVALID_VALUE;
+  if (ws && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return LPGEMM_ERROR_MISALIGNED;
   DeviceInfo dev;
   st = current_device(dev);
   if (st != LPGEMM_SUCCESS) return st;
@@ -37,9 +41,16 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   const int64_t row_bytes = KIND == KIND_F16 ? 2 * K : (KIND == KIND_I4 ? K / 2 : K);
   args.row_bytes = (int)row_bytes;
 
-  const KernelCfg cfg = BKN ? choose_config_kxn(M, N, dev.cu_count)
-                      : (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) ? choose_config_e3m2(M, N, dev.cu_count)
-                                             : choose_config(M, N, dev.cu_count, KIND);
+  KernelCfg cfg = BKN ? choose_config_kxn(M, N, dev.cu_count)
+                : (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) ? choose_config_e3m2(M, N, dev.cu_count)
+                                                                : choose_config(M, N, dev.cu_count, KIND);
+  // split-K: on the automatic choice, products with few 128 x 128 tiles and
+  // a long K split it when the caller gave a workspace
+  constexpr bool kCanSplit = !BKN && KIND != KIND_I4_E3M2 && KIND != KIND_I8_MOD;
+  const int split_nks = (int)((row_bytes + 255) / 256);
+  if (kCanSplit && forced_config() < 0 && splitk_auto_splits(M, N, split_nks, dev.cu_count) > 1 &&
+      splitk_launch_splits(M, N, split_nks, dev.cu_count, ws, ws_bytes) > 1)
+    cfg = CFG_128_S2_R256_SPLITK;
   const int64_t stage_bytes = (KIND == KIND_I4 && expands_int4_in_lds(cfg)) ? K : row_bytes;
   const int rowb = stage_row_bytes(cfg);
   args.k_stages = (int)((stage_bytes + rowb - 1) / rowb);
@@ -153,6 +164,14 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
             args, 256, stream);
     case CFG_REF:
       return launch<128, 128>((const void*)&gemm_ref<KIND>, args, 256, stream);
+    case CFG_128_S2_R256_SPLITK:
+      if constexpr (kCanSplit)
+        return launch_split<128, 128>(
+            (const void*)&gemm_v3<KIND, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, kI4(1),
+                                  false, true>,
+            args, 256, stream, splitk_launch_splits(M, N, args.k_stages, dev.cu_count, ws, ws_bytes), ws);
+      else
+        return LPGEMM_ERROR_LAUNCH;
     case CFG_256_S4_R64:
       return launch<256, 256>((const void*)&gemm_v3<KIND, 256, 256, 4, 64>, args, 256, stream);
     case CFG_256_S3_R64:

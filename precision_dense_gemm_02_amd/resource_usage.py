@@ -21,16 +21,20 @@ from .build import FLAGS, HIPCC, _jobs, sources
 # kernels launched by the automatic choice (the name's prefix up to the
 # closing template bracket), and the workloads that run them
 DEFAULT_KERNELS = {
-    "lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false>": "int8, >= 2 rounds of 256x256 tiles (8192^3), persistent",
-    "lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false, 0, false>": "int8, 1-2 rounds of 256x256 tiles (4096^3)",
-    "lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false, false, 0, false>": "int4, >= 1 round of 256x256 tiles",
-    "lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false>": "fp16, >= 2 rounds (8192^3), persistent",
-    "lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false, 0, false>": "fp16, 1-2 rounds (4096^3)",
-    "lpgemm::gemm_v3<3, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false, 0, false>": "dequant int8 (LLM M = 2048)",
-    "lpgemm::gemm_v3<0, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false>": "int8, 128x128 tiles (2048^3)",
-    "lpgemm::gemm_v3<2, 128, 128, 4, 128, 0, false, false, 0, false, 0, false, false, false, 0, false>": "fp16, 128x128 tiles (2048^3)",
-    "lpgemm::gemm_v3<1, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 1, false>": "int4, 128x128 tiles (2048^3), 32-byte fragment reads",
-    "lpgemm::gemm_v3<3, 128, 64, 3, 256, 0, false, false, 0, false, 0, false, false, false, 0, false>": "dequant int8, M <= 128 (LLM M = 128)",
+    "lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false, false>": "int8, >= 2 rounds of 256x256 tiles (8192^3), persistent",
+    "lpgemm::gemm_v3<0, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false, 0, false, false>": "int8, 1-2 rounds of 256x256 tiles (4096^3)",
+    "lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false, false, 0, false, false>": "int4, >= 1 round of 256x256 tiles",
+    "lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false, false>": "fp16, >= 2 rounds (8192^3), persistent",
+    "lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false, 0, false, false>": "fp16, 1-2 rounds (4096^3)",
+    "lpgemm::gemm_v3<3, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false, 0, false, false>": "dequant int8 (LLM M = 2048)",
+    "lpgemm::gemm_v3<0, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "int8, 128x128 tiles (2048^3)",
+    "lpgemm::gemm_v3<2, 128, 128, 4, 128, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "fp16, 128x128 tiles (2048^3)",
+    "lpgemm::gemm_v3<1, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 1, false, false>": "int4, 128x128 tiles (2048^3), 32-byte fragment reads",
+    "lpgemm::gemm_v3<3, 128, 64, 3, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "dequant int8, M <= 128 (LLM M = 128)",
+    "lpgemm::gemm_v3<0, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, true>": "int8 split-K (few tiles, long K)",
+    "lpgemm::gemm_v3<1, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 1, false, true>": "int4 split-K",
+    "lpgemm::gemm_v3<2, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, true>": "fp16 split-K",
+    "lpgemm::gemm_v3<3, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, true>": "dequant int8 split-K",
     "lpgemm::gemm_skinny_pipe<3, 4, 2, false>": "dequant int8, M <= 32 (LLM M = 16)",
     "lpgemm::gemm_tiled<0, 64, 64, 2, 2>": "int8, small grids (1024^3, 512^3)",
     "lpgemm::quantize_rows_f16_regs<4, 2>": "W8A8 row quantiser, short M",

@@ -29,14 +29,27 @@ def test_more_than_one_gpu_is_refused():
     ("llm-16", ("dq", 16, 14336, 4096)),
     ("w8a8-128", ("w8", 128, 14336, 4096)),
     ("w8a8f-16", ("w8f", 16, 14336, 4096)),
+    ("i8-1024x1024x8192", ("i8", 1024, 1024, 8192)),
+    ("i8sk-512x2048x32768", ("i8", 512, 2048, 32768)),
+    ("f16sk-300x520x8208", ("f16", 300, 520, 8208)),
+    ("dqsk-256x4096x8192", ("dq", 256, 4096, 8192)),
+    ("i4sk-4096", ("i4", 4096, 4096, 4096)),
 ])
 def test_parse_workload(name, expect):
     assert bench.parse_workload(name) == expect
 
 
-def test_unknown_workload_is_rejected():
+def test_split_kind():
+    assert bench.split_kind("i8sk-512x2048x32768") == ("i8", True)
+    assert bench.split_kind("i4sk-4096") == ("i4", True)
+    assert bench.split_kind("i8-8192") == ("i8", False)
+    assert bench.split_kind("llm-128") == ("llm", False)
+
+
+@pytest.mark.parametrize("name", ["bf16-8192", "i8-1x2", "llm-1x2x3", "i8sk-1x2x", "i8-8192-1", "i8-x"])
+def test_unknown_workload_is_rejected(name):
     with pytest.raises(SystemExit):
-        bench.parse_workload("bf16-8192")
+        bench.parse_workload(name)
 
 
 def _workload(name, kind, M, N, K, in_bytes, out_bytes):

@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol(lib):
                           "lpgemm_f64_emu_moduli",
                           "lpgemm_f64_emu_workspace",
                           "lpgemm_status_string", "lpgemm_version", "lpgemm_config_count",
-                          "lpgemm_force_config"}
+                          "lpgemm_force_config", "lpgemm_splitk_workspace", "lpgemm_i8_splitk",
+                          "lpgemm_i4_splitk", "lpgemm_f16_splitk", "lpgemm_i8_dequant_splitk"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -46,23 +47,33 @@ def test_config_count_and_force_hook(lib):
 
 
 def test_version_and_strings(lib):
-    assert b.version() == 200
+    assert b.version() == 300
     for code in range(6):
         assert b.status_string(code)
     assert b.status_string(99) == "unknown status"
 
 
-def _call(lib, name, M, N, K, A=FAKE, B=FAKE, C=FAKE, rs=FAKE, cs=FAKE):
+WS = 0x20000       # 256-byte aligned, never dereferenced
+WS_BYTES = 1 << 30
+
+
+def _call(lib, name, M, N, K, A=FAKE, B=FAKE, C=FAKE, rs=FAKE, cs=FAKE, ws=WS, ws_bytes=WS_BYTES):
     # lpgemm_i4_e3m2 has lpgemm_i4's signature and rules; lpgemm_i8_kxn
-    # lpgemm_i8's, plus N % 16 == 0 (the generic cases use N = 4 -> 16)
+    # lpgemm_i8's, plus N % 16 == 0 (the generic cases use N = 4 -> 16); the
+    # split-K entry points those of their unsuffixed kind, plus a workspace
     if name == "lpgemm_i8_kxn" and N == 4:
         N = 16
     if name == "lpgemm_i8_dequant":
         return lib.lpgemm_i8_dequant(M, N, K, A, B, rs, cs, C, None)
+    if name == "lpgemm_i8_dequant_splitk":
+        return lib.lpgemm_i8_dequant_splitk(M, N, K, A, B, rs, cs, C, ws, ws_bytes, None)
+    if name.endswith("_splitk"):
+        return getattr(lib, name)(M, N, K, A, B, C, ws, ws_bytes, None)
     return getattr(lib, name)(M, N, K, A, B, C, None)
 
 
-ALL = ENTRY + ("lpgemm_i8_dequant", "lpgemm_i4_e3m2", "lpgemm_i8_kxn")
+SPLITK = ("lpgemm_i8_splitk", "lpgemm_i4_splitk", "lpgemm_f16_splitk", "lpgemm_i8_dequant_splitk")
+ALL = ENTRY + ("lpgemm_i8_dequant", "lpgemm_i4_e3m2", "lpgemm_i8_kxn") + SPLITK
 K_OK = {"lpgemm_i8": 64, "lpgemm_i4": 64, "lpgemm_f16": 64, "lpgemm_i8_dequant": 64}
 
 
@@ -75,6 +86,10 @@ def test_negative_sizes(lib, name):
 
 @pytest.mark.parametrize("name,bad_k", [
     ("lpgemm_i8", [8, 17, 131072, 131088]),
+    ("lpgemm_i8_splitk", [8, 17, 131072, 131088]),
+    ("lpgemm_i4_splitk", [16, 48, 131072]),
+    ("lpgemm_f16_splitk", [4, 12, 1048584]),
+    ("lpgemm_i8_dequant_splitk", [8, 24, 131072]),
     ("lpgemm_i8_dequant", [8, 24, 131072]),
     ("lpgemm_i4", [16, 48, 131072, 131104]),
     ("lpgemm_i4_e3m2", [16, 48, 131072, 131104]),
@@ -95,9 +110,28 @@ def test_null_pointers(lib, name):
     assert _call(lib, name, 4, 4, 0, C=None) == b.LPGEMM_ERROR_INVALID_VALUE
 
 
-def test_null_scales(lib):
-    assert _call(lib, "lpgemm_i8_dequant", 4, 4, 64, rs=None) == b.LPGEMM_ERROR_INVALID_VALUE
-    assert _call(lib, "lpgemm_i8_dequant", 4, 4, 64, cs=None) == b.LPGEMM_ERROR_INVALID_VALUE
+@pytest.mark.parametrize("name", ["lpgemm_i8_dequant", "lpgemm_i8_dequant_splitk"])
+def test_null_scales(lib, name):
+    assert _call(lib, name, 4, 4, 64, rs=None) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert _call(lib, name, 4, 4, 64, cs=None) == b.LPGEMM_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("name", SPLITK)
+def test_splitk_workspace_checks(lib, name):
+    # after the unsuffixed entry point's checks, before the device
+    assert _call(lib, name, 4, 4, 64, ws_bytes=-1) == b.LPGEMM_ERROR_INVALID_VALUE
+    assert _call(lib, name, 4, 4, 64, ws=WS + 16) == b.LPGEMM_ERROR_MISALIGNED
+    assert _call(lib, name, 4, 4, 64, A=MISALIGNED, ws_bytes=-1) == b.LPGEMM_ERROR_MISALIGNED
+    bad_k = {"lpgemm_i4_splitk": 48, "lpgemm_f16_splitk": 12}.get(name, 24)
+    assert _call(lib, name, 4, 4, bad_k, ws_bytes=-1) == b.LPGEMM_ERROR_UNSUPPORTED_SHAPE
+    # an empty product reads no pointer, the workspace included
+    assert _call(lib, name, 0, 4, 64, A=None, B=None, C=None, rs=None, cs=None, ws=WS + 16, ws_bytes=-1) == 0
+
+
+def test_splitk_workspace_query_bad_sizes(lib):
+    assert lib.lpgemm_splitk_workspace(-1, 16) == -1
+    assert lib.lpgemm_splitk_workspace(16, -1) == -1
+    assert lib.lpgemm_splitk_workspace(2 ** 31, 16) == -1
 
 
 @pytest.mark.parametrize("name", ALL)

@@ -40,6 +40,7 @@ import json
 import os
 import sys
 import time
+from typing import Optional
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -110,10 +111,26 @@ def parse_workload(name: str):
     return base, size, size, size
 
 
-class Workload:
-    """Inputs on the device and a closure that launches one GEMM."""
+# Bytes of rotating input copies that keep a "cold" workload's operands out
+# of the 256 MB Infinity Cache: each launch reads a copy last touched at
+# least this many bytes of operand reads earlier.
+COLD_ROTATION_BYTES = 336 * 2 ** 20
 
-    def __init__(self, name: str):
+
+def default_cache(name: str) -> str:
+    """The LLM and W8A8 workloads stream their weights cold (rotating copies);
+    every other workload reuses one resident copy (warm)."""
+    return "cold" if name.split("-", 1)[0] in ("llm", "w8a8", "w8a8f") else "warm"
+
+
+class Workload:
+    """Inputs on the device and a closure that launches one GEMM.  `cache`:
+    "warm" launches read one resident copy of the operands; "cold" ones
+    rotate over copies totalling COLD_ROTATION_BYTES (for the i8, i4, f16
+    and dequant kinds and the W8A8 weights), so every launch reads its
+    operands from HBM."""
+
+    def __init__(self, name: str, cache: Optional[str] = None):
         import numpy as np
         import torch
 
@@ -124,11 +141,22 @@ class Workload:
         self.kind, M, N, K = parse_workload(name)
         self.M, self.N, self.K = M, N, K
         self.split = split_kind(name)[1]
+        self.cache = cache or default_cache(name)
+        if self.cache not in ("warm", "cold"):
+            raise ValueError(f"cache must be warm or cold, not {self.cache}")
         dev = torch.device("cuda:0")
 
         def to(x):
             return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
+        def copies(nbytes: int) -> int:
+            return max(1, -(-COLD_ROTATION_BYTES // nbytes)) if self.cache == "cold" else 1
+
+        def sets_of(*host, nbytes: int) -> list:
+            # identical device copies of the operands, one per rotation slot
+            return [tuple(to(x) for x in host) for _ in range(copies(nbytes))]
+
+        self.sets = 1   # rotating input copies (cold workloads)
         # split-K forms: the same inputs through the *_splitk entry point,
         # with a workspace zeroed once here
         ws_k = lp.splitk_workspace(M, N) if self.split else None
@@ -137,12 +165,13 @@ class Workload:
             self.seed = inputs.seed_for("i8", M)
             p = inputs.int8_problem(M, N, K, self.seed)
             self.host = p
-            a, b = to(p.a), to(p.b_t)
+            S = sets_of(p.a, p.b_t, nbytes=M * K + N * K)
+            self.sets = len(S)
             out = torch.empty((M, N), dtype=torch.int32, device=dev)
             if self.split:
-                self.launch = lambda i: lp.gemm_i8_splitk(a, b, ws_k, out=out)
+                self.launch = lambda i: lp.gemm_i8_splitk(*S[i % len(S)], ws_k, out=out)
             else:
-                self.launch = lambda i: lp.gemm_i8(a, b, out=out)
+                self.launch = lambda i: lp.gemm_i8(*S[i % len(S)], out=out)
             self.in_bytes = M * K + N * K
             self.out_bytes = 4 * M * N
         elif kind == "f64e":
@@ -178,12 +207,13 @@ class Workload:
             self.seed = inputs.seed_for("i4", M)
             p = inputs.int4_problem(M, N, K, self.seed)
             self.host = p
-            a, b = to(p.a_packed), to(p.b_packed)
+            S = sets_of(p.a_packed, p.b_packed, nbytes=(M * K + N * K) // 2)
+            self.sets = len(S)
             out = torch.empty((M, N), dtype=torch.int32, device=dev)
             if self.split:
-                self.launch = lambda i: lp.gemm_i4_splitk(a, b, ws_k, K, out=out)
+                self.launch = lambda i: lp.gemm_i4_splitk(*S[i % len(S)], ws_k, K, out=out)
             else:
-                self.launch = lambda i: lp.gemm_i4(a, b, K, out=out)
+                self.launch = lambda i: lp.gemm_i4(*S[i % len(S)], K, out=out)
             self.in_bytes = (M * K + N * K) // 2
             self.out_bytes = 4 * M * N
         elif kind in ("i4e", "i4g"):
@@ -213,12 +243,13 @@ class Workload:
             self.seed = inputs.seed_for("f16", M)
             p = inputs.f16_problem(M, N, K, self.seed)
             self.host = p
-            a, b = to(p.a), to(p.b_t)
+            S = sets_of(p.a, p.b_t, nbytes=2 * (M * K + N * K))
+            self.sets = len(S)
             out = torch.empty((M, N), dtype=torch.float32, device=dev)
             if self.split:
-                self.launch = lambda i: lp.gemm_f16_splitk(a, b, ws_k, out=out)
+                self.launch = lambda i: lp.gemm_f16_splitk(*S[i % len(S)], ws_k, out=out)
             else:
-                self.launch = lambda i: lp.gemm_f16(a, b, out=out)
+                self.launch = lambda i: lp.gemm_f16(*S[i % len(S)], out=out)
             self.in_bytes = 2 * (M * K + N * K)
             self.out_bytes = 4 * M * N
         elif kind == "w8f":
@@ -227,8 +258,8 @@ class Workload:
             p = inputs.w8a8_problem(M, N, K, self.seed)
             self.host = p
             x, ws = to(p.x), to(p.w_scale)
-            copies = max(1, -(-336 * 2 ** 20 // (N * K)))
-            ws_list = [to(p.w) for _ in range(copies)]
+            ws_list = [to(p.w) for _ in range(copies(N * K))]
+            self.sets = len(ws_list)
             out = torch.empty((M, N), dtype=torch.float32, device=dev)
             self.launch = lambda i: lp.w8a8_linear_fused(x, ws_list[i % len(ws_list)], ws, out=out)
             self.in_bytes = 2 * M * K + N * K + 4 * N
@@ -240,8 +271,8 @@ class Workload:
             p = inputs.w8a8_problem(M, N, K, self.seed)
             self.host = p
             x, ws = to(p.x), to(p.w_scale)
-            copies = max(1, -(-336 * 2 ** 20 // (N * K)))
-            ws_list = [to(p.w) for _ in range(copies)]
+            ws_list = [to(p.w) for _ in range(copies(N * K))]
+            self.sets = len(ws_list)
             q = torch.empty((M, K), dtype=torch.int8, device=dev)
             s = torch.empty((M,), dtype=torch.float32, device=dev)
             out = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -260,9 +291,9 @@ class Workload:
                 p = inputs.int8_problem(M, N, K, self.seed, scales=True)
             self.host = p
             a, rs, cs = to(p.a), to(p.row_scale), to(p.col_scale)
-            # rotate weight copies so that the timed launches stream B from HBM
-            copies = max(1, -(-336 * 2 ** 20 // (N * K)))
-            bs = [to(p.b_t)] + [to(p.b_t) for _ in range(copies - 1)]
+            # cold: rotate weight copies so that the timed launches stream B from HBM
+            bs = [to(p.b_t) for _ in range(copies(N * K))]
+            self.sets = len(bs)
             out = torch.empty((M, N), dtype=torch.float32, device=dev)
             if self.split:
                 self.launch = lambda i: lp.gemm_i8_dequant_splitk(a, bs[i % len(bs)], rs, cs, ws_k, out=out)
@@ -326,11 +357,14 @@ def settle(launch, seconds: float) -> dict:
 def time_graph(w: Workload, steps: int, warmup: int, settle_s: float) -> dict:
     """Capture `steps` launches in one HIP graph and time its replay: GPU time
     only, without the host's per-call overhead (which dominates below about
-    20 us per GEMM).  The settle phase replays the graph."""
+    20 us per GEMM).  The settle phase replays the graph.  A cold workload's
+    graph holds at least one launch per rotating input copy, so that every
+    replayed launch reads a copy last touched a whole rotation earlier."""
     import torch
     for i in range(max(warmup, 3)):
         w.launch(i)
     torch.cuda.synchronize()
+    steps = max(steps, w.sets)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(steps):
@@ -352,8 +386,12 @@ def time_workload(w: Workload, steps: int, warmup: int, settle_s: float) -> dict
     import torch
     stream = torch.cuda.current_stream()
     st = settle(w.launch, settle_s)
+    # launch indices run on from the settle phase, so that a cold workload's
+    # warm-up and timed launches keep rotating through its input copies
+    first = st["settle_launches"]
     for i in range(warmup):
-        w.launch(i)
+        w.launch(first + i)
+    first += warmup
     torch.cuda.synchronize()
     region0 = torch.cuda.Event(enable_timing=True)
     region1 = torch.cuda.Event(enable_timing=True)
@@ -363,7 +401,7 @@ def time_workload(w: Workload, steps: int, warmup: int, settle_s: float) -> dict
     region0.record(stream)
     for i in range(steps):
         pairs[i][0].record(stream)
-        w.launch(i)
+        w.launch(first + i)
         pairs[i][1].record(stream)
     region1.record(stream)
     torch.cuda.synchronize()
@@ -472,13 +510,15 @@ def f64e_report(w, steps: int, warmup: int) -> dict:
                               "how": "torch.matmul on float64 (the platform library)"}}
 
 
-def measure(name: str, steps: int, warmup: int, graph: bool = False, settle_s: float = 1.0) -> tuple:
-    w = Workload(name)
+def measure(name: str, steps: int, warmup: int, graph: bool = False, settle_s: float = 1.0,
+            cache: Optional[str] = None) -> tuple:
+    w = Workload(name, cache)
     t = time_graph(w, steps, warmup, settle_s) if graph else time_workload(w, steps, warmup, settle_s)
     r = roofline(w, t)
     value = w.ops / (t["ms_per_step"] / 1e3) / 1e12
     rec = {"workload": name, "value": round(value, 1), "unit": UNIT[w.kind],
            "timing": "hip graph replay" if graph else "eager launches",
+           "cache": w.cache, "input_copies": w.sets,
            "ms_per_step": round(t["ms_per_step"], 5),
            "kernel_ms_avg": round(t["kernel_ms_avg"], 5),
            "kernel_ms_min": round(t["kernel_ms_min"], 5),
@@ -665,11 +705,21 @@ def main():
         sw, rec = measure(name, args.sweep_steps, args.warmup, True, args.sweep_settle_seconds)
         if not args.no_cpu_baseline:
             rec["cpu_baseline"] = cpu_baseline(sw, args.sweep_cpu_seconds)
+        if rec["roofline"]["bound"] == "hbm":
+            # HBM-bound shapes are reported with the operands both in and out
+            # of the Infinity Cache (the first measurement's inputs freed first)
+            del sw
+            other = "warm" if rec["cache"] == "cold" else "cold"
+            _, o = measure(name, args.sweep_steps, args.warmup, True, args.sweep_settle_seconds, cache=other)
+            rec["other_cache"] = {k: o[k] for k in ("cache", "input_copies", "value", "ms_per_step",
+                                                    "kernel_ms_avg", "roofline", "parity")}
         print(f"# sweep {rec['workload']}: {rec['value']} {rec['unit']}, roofline "
-              f"{rec['roofline']['frac']} of {rec['roofline']['bound']} ({rec['parity']})",
+              f"{rec['roofline']['frac']} of {rec['roofline']['bound']} ({rec['parity']})"
+              + (f"; {rec['other_cache']['cache']}: {rec['other_cache']['value']} {rec['unit']}"
+                 if "other_cache" in rec else ""),
               file=sys.stderr, flush=True)
         also.append(rec)
-        del sw
+        sw = None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)

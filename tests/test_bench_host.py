@@ -127,3 +127,14 @@ def test_write_traffic_scales_by_the_copy_and_checks_the_hash(tmp_path, monkeypa
     assert bench.roofline(w, {"kernel_ms_avg": 0.5})["traffic"] == first["fetch_bytes"] + first["write_bytes"]
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
     assert bench.roofline(w, {"kernel_ms_avg": 0.5})["traffic"] is None
+
+
+def test_default_cache_state():
+    # the LLM and W8A8 weights stream cold (rotating copies); the rest warm
+    assert bench.default_cache("llm-16") == "cold"
+    assert bench.default_cache("w8a8-128") == "cold"
+    assert bench.default_cache("w8a8f-16") == "cold"
+    for name in ("i8-512", "f16-8192", "i4-2048", "i8sk-300x520x8208", "dq-256x4096x8192"):
+        assert bench.default_cache(name) == "warm", name
+    # enough copies to exceed the 256 MB Infinity Cache
+    assert bench.COLD_ROTATION_BYTES > 256 * 10 ** 6

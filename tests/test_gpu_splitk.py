@@ -299,3 +299,26 @@ def test_graph_replays():
     rows = [0, 77, 127]
     ref = oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale, rows=rows)
     np.testing.assert_array_equal(eager.cpu().numpy()[rows].view(np.uint32), ref.view(np.uint32))
+
+
+def test_two_streams_two_workspaces():
+    # split-K products in flight together on two streams, each with its own
+    # workspace, repeatedly: no cross-talk between the workspaces' counters
+    # or slots, and each stream's results stay exact
+    _say("split-K two streams")
+    shapes = [(300, 520, 8208), (200, 3000, 8208)]
+    probs = [inputs.int8_problem(M, N, K, seed=40 + i) for i, (M, N, K) in enumerate(shapes)]
+    dev = [(_dev(p.a), _dev(p.b_t)) for p in probs]
+    wss = [lp.splitk_workspace(M, N) for (M, N, _) in shapes]
+    outs = [torch.empty((M, N), dtype=torch.int32, device="cuda") for (M, N, _) in shapes]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(10):
+        for s, (a, b), ws, out in zip(streams, dev, wss, outs):
+            with torch.cuda.stream(s):
+                lp.gemm_i8_splitk(a, b, ws, out=out)
+    torch.cuda.synchronize()
+    for p, out, ws, (M, N, K) in zip(probs, outs, wss, shapes):
+        rows = None if M * N * K < 2 ** 31 else [0, 1, M // 2, M - 1]
+        _check_i8(out, p, rows)
+        assert _counters_zero(ws)

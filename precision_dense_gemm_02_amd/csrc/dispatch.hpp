@@ -200,6 +200,12 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
   if (mid >= cu_count / 2)
     return kind == KIND_F16 ? CFG_128_S4_R128 : (kind == KIND_I4 ? CFG_128_S2_R256_W4 : CFG_128_S2_R256);
+  // fewer 64 x 64 tiles than half the CUs: 32 x 32 tiles whose eight waves
+  // split K, four times the workgroups (graph-timed, one MI355X: int8 512^3
+  // 2.89 against 3.53 us, int4 2.87 against 3.79, fp16 3.43 against 4.70;
+  // int8 512 x 512 x 16384 21.7 against 63.8 us; 768^3, with 144 tiles,
+  // stays faster on 64 x 64: 4.23 against 5.26 us)
+  if ((int64_t)tiles(M, 64) * tiles(N, 64) <= cu_count / 2) return CFG_SKINNY_PIPE_W8R1;
   return CFG_V1_64x64;
 }
 
@@ -211,13 +217,14 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
 // hand-over (the parts written through to the device's coherence point, an
 // arrival counter, the parts read back) costs a few microseconds per tile,
 // so the automatic choice splits only products whose 128 x 128 tiles fill
-// at most a quarter of the CUs, four ways, and only when K spans at least
-// 32 K-stages of 256 bytes (8 per part).  Measured (graph replay, one
-// MI355X): int8 512 x 2048 x 32768 2.5 times, 256 x 4096 x 16384 2.0 times,
-// 1024 x 1024 x 8192 1.5 times, 300 x 520 x 8208 1.2 times as fast; fp16
-// 1024 x 1024 x 8192 1.9 times; int4 1024 x 1024 x 16384 2.3 times.  Two
-// parts of 8 stages lost: int8 1024 x 1024 x 4096 16.4 against 12.8 us,
-// the LLM projection at M = 128, K = 4096 (112 tiles) 23 against 18 us.
+// at most a quarter of the CUs (see splitk_auto_shape), four ways, and only
+// when K spans at least 32 K-stages of 256 bytes (8 per part).  Measured
+// (graph replay, one MI355X): int8 512 x 2048 x 32768 2.5 times, 256 x 4096
+// x 16384 2.0 times, 1024 x 1024 x 8192 1.5 times as fast as the 64 x 64
+// kernel; fp16 1024 x 1024 x 8192 1.9 times; int4 1024 x 1024 x 16384 2.3
+// times.  Two parts of 8 stages lost: int8 1024 x 1024 x 4096 16.4 against
+// 12.8 us, the LLM projection at M = 128, K = 4096 (112 tiles) 23 against
+// 18 us.
 //
 // Workspace layout, the same for every shape so that one workspace serves
 // products of any size in turn: 4 KiB of 32-bit arrival counters (tile t
@@ -238,9 +245,14 @@ inline int64_t splitk_bytes(int64_t ntiles, int splits) {
 // Whether the automatic choice splits an M x N product on `cu_count` CUs
 // at all (any K): above 64 rows (below that the skinny kernels split K
 // inside a workgroup) and when the 128 x 128 tiles fill at most a quarter
-// of the CUs.  Such a product may use up to kMaxSplits parts.
+// of the CUs, but not above 128 rows with at most a quarter of the CUs'
+// worth of 64 x 64 tiles, where the unsplit choice (32 x 32 tiles whose
+// waves split K) was as fast or faster (int8 512 x 512 x 16384: 21.7
+// against 23.4 us split; 300 x 520 x 8208: 16.6 against 18.4 us).  Such a
+// product may use up to kMaxSplits parts.
 inline bool splitk_auto_shape(int64_t M, int64_t N, int cu_count) {
-  return M > 64 && (int64_t)tiles(M, kSplitTile) * tiles(N, kSplitTile) <= cu_count / 4;
+  if (M <= 64 || (int64_t)tiles(M, kSplitTile) * tiles(N, kSplitTile) > cu_count / 4) return false;
+  return M <= 128 || (int64_t)tiles(M, 64) * tiles(N, 64) > cu_count / 4;
 }
 
 // Parts for the automatic choice with `nks` 256-byte K-stages (1: no split).

@@ -43,11 +43,19 @@ def _tiles(M, N):
     return ((M + 127) // 128) * ((N + 127) // 128)
 
 
-def _expected_splits(M, N, row_bytes):
+def _tiles64(M, N):
+    return ((M + 63) // 64) * ((N + 63) // 64)
+
+
+def _split_shape(M, N):
     # the library's rule on 256 CUs: M > 64, at most 64 tiles of 128 x 128,
-    # and at least 32 K-stages of 256 bytes: then 4 parts
-    t = _tiles(M, N)
-    if M <= 64 or t > 64:
+    # and above 128 rows more than 64 tiles of 64 x 64
+    return M > 64 and _tiles(M, N) <= 64 and (M <= 128 or _tiles64(M, N) > 64)
+
+
+def _expected_splits(M, N, row_bytes):
+    # ... and at least 32 K-stages of 256 bytes: then 4 parts
+    if not _split_shape(M, N):
         return 1
     return 4 if (row_bytes + 255) // 256 >= 32 else 1
 
@@ -57,19 +65,21 @@ def _counters_zero(ws, M=None, N=None):
     return bool((ws[:4096].view(torch.int32) == 0).all().item())
 
 
-# int8 (row bytes = K) splits four ways on 256 CUs: 15 tiles of 33
+# int8 (row bytes = K) splits four ways on 256 CUs: 40 tiles of 33
 # K-stages, 32 tiles of 64, 48 tiles of 33 (fp16 rows are twice as long;
 # int4 rows half as long, so only the second shape splits for int4).  Ragged
 # M, N and K (a last stage that runs past K) throughout.
-SHAPES = [(300, 520, 8208), (128, 4096, 16384), (200, 3000, 8208)]
+SHAPES = [(600, 1000, 8208), (128, 4096, 16384), (200, 3000, 8208)]
 
 
 def test_workspace_query_matches_rule():
-    for M, N in [(300, 520), (1000, 1000), (200, 3000), (128, 4096), (64, 4096), (128, 14336), (2048, 2048)]:
+    for M, N in [(300, 520), (600, 1000), (1000, 1000), (200, 3000), (128, 4096), (64, 4096), (128, 14336),
+                 (2048, 2048), (512, 512)]:
         t = _tiles(M, N)
-        want = 0 if (M <= 64 or t > 64) else 4096 + t * 4 * SLOT
+        want = 4096 + t * 4 * SLOT if _split_shape(M, N) else 0
         assert lp.splitk_workspace_bytes(M, N) == want, (M, N)
     assert lp.splitk_workspace_bytes(128, 14336) == 0   # 112 tiles: no split
+    assert lp.splitk_workspace_bytes(300, 520) == 0     # 45 tiles of 64 x 64: the unsplit kernel splits K itself
     assert [_expected_splits(M, N, K) for M, N, K in SHAPES] == [4, 4, 4]
     assert [_expected_splits(M, N, K // 2) for M, N, K in SHAPES] == [1, 4, 1]
 
@@ -172,27 +182,29 @@ def test_workspace_reuse_across_shapes_and_small_workspace():
     # zero after each call); a workspace one byte short runs the product
     # unsplit without touching it
     ws = lp.splitk_workspace(1000, 1000)
-    for (m, n, k, rows) in [(300, 520, 8208, None), (1000, 1000, 8208, [0, 1, 500, 998, 999]),
-                            (300, 520, 256, None), (200, 130, 8192, None), (300, 520, 8208, None)]:
+    for (m, n, k, rows) in [(600, 1000, 8208, [0, 1, 300, 599]), (1000, 1000, 8208, [0, 1, 500, 998, 999]),
+                            (300, 520, 256, None), (128, 4096, 16384, [0, 64, 127]),
+                            (600, 1000, 8208, [0, 2, 301, 599])]:
         _say("split-K reuse", m, n, k, "splits", _expected_splits(m, n, k))
         p = inputs.int8_problem(m, n, k, seed=m + n + k + 1 + (rows is None))
         got = lp.gemm_i8_splitk(_dev(p.a), _dev(p.b_t), ws)
         torch.cuda.synchronize()
         _check_i8(got, p, rows)
         assert _counters_zero(ws)
-    M, N, K = 300, 520, 8208
+    M, N, K = 600, 1000, 8208
     p = inputs.int8_problem(M, N, K, seed=9)
     short = torch.zeros(lp.splitk_workspace_bytes(M, N) - 1, dtype=torch.uint8, device="cuda")
     got = lp.gemm_i8_splitk(_dev(p.a), _dev(p.b_t), short)
     torch.cuda.synchronize()
-    _check_i8(got, p)
+    _check_i8(got, p, [0, 1, 599])
     assert bool((short == 0).all().item())
 
 
 def test_edge_cases():
     # K = 0 (zeros), K of one stage (cannot split), M <= 64 (the skinny
     # kernel), M = 65 (one edge row past a full band, split four ways)
-    ws = lp.splitk_workspace(300, 520)
+    ws = lp.splitk_workspace(128, 4096)
+    assert _expected_splits(65, 520, 8192) == 4
     for (M, N, K) in [(300, 520, 0), (300, 520, 256), (64, 520, 8192), (65, 520, 8192), (1, 1, 16)]:
         _say("split-K edge", M, N, K, "splits", _expected_splits(M, N, K))
         p = inputs.int8_problem(M, N, K, seed=M + N + K + 2)
@@ -306,7 +318,7 @@ def test_two_streams_two_workspaces():
     # workspace, repeatedly: no cross-talk between the workspaces' counters
     # or slots, and each stream's results stay exact
     _say("split-K two streams")
-    shapes = [(300, 520, 8208), (200, 3000, 8208)]
+    shapes = [(600, 1000, 8208), (200, 3000, 8208)]
     probs = [inputs.int8_problem(M, N, K, seed=40 + i) for i, (M, N, K) in enumerate(shapes)]
     dev = [(_dev(p.a), _dev(p.b_t)) for p in probs]
     wss = [lp.splitk_workspace(M, N) for (M, N, _) in shapes]

@@ -199,9 +199,11 @@ lpgemm_status lpgemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A
  *   is (0 when that product never splits; -1 for sizes outside 0..2^31-1
  *   or when the device cannot be queried).
  * The automatic choice splits when M > 64, the product's 128 x 128 output
- * tiles number at most a quarter of the GPU's compute units, and each
- * operand row holds more than 31 x 256 bytes (int8 K >= 7952, fp16
- * K >= 3976, int4 K >= 15904).  The K dimension of each tile is then split
+ * tiles number at most a quarter of the GPU's compute units, for M > 128
+ * its 64 x 64 tiles number more than a quarter of them (below that the
+ * unsplit kernel already splits K inside each workgroup), and each operand
+ * row holds more than 31 x 256 bytes (int8 K >= 7952, fp16 K >= 3976, int4
+ * K >= 15904).  The K dimension of each tile is then split
  * over 4 workgroups; each writes its partial sums to the workspace and the
  * last of a tile to finish adds them and writes C.
  * The integer results are exact and equal to the unsplit entry point's bit

@@ -136,7 +136,9 @@ enum KernelCfg {
   CFG_256_S2_R128_EARLY = 58,    // configuration 0 with half of each stage's loads issued one K-step earlier
   CFG_128_S2_R256_BIAS = 59,     // configuration 36, int4 expanded biased (u = v + 8) with sum corrections
   CFG_128_S2_R256_SPLITK = 60,   // configuration 36 (int4: 48) with K split over workgroups (needs a workspace)
-  CFG_COUNT = 61
+  CFG_256x224_S2_R128 = 61,      // configuration 0 with 256 x 224 tiles (four waves of 64 x 224)
+  CFG_256x224_S2_R128_PERSIST = 62,  // configuration 61 as a persistent grid (int4: 61)
+  CFG_COUNT = 63
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -186,6 +188,20 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   // N = 14336: 19.2 us against 20.4 us with six 128-byte stages)
   if (M <= 128) return int8_rows ? CFG_128x64_S3_R256 : CFG_128x64_S6_R128;
   const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
+  // N a multiple of 224 (the LLM projection's 14336 = 64 x 224): 256 x 224
+  // tiles when their rounds of one tile per CU, each 7/8 of a 256 x 256
+  // round's work, add up to less (M = 2048: 512 tiles in two full rounds
+  // against 448 in 1.75), on the persistent grid from two rounds on (int4:
+  // the plain grid).  Graph-timed, K = 4096, int8, plain 224 grid: M = 2048
+  // 2173 TOP/s against 2152 with 256 x 256 tiles (1.75 rounds), M = 4096
+  // 2156 against 2064 on the persistent 256 x 256 grid (3.5 rounds), one
+  // MI355X; on another, the persistent 224 grid 2-3.5% ahead of the plain
+  // one at both sizes and at M = 6144 (dequant and fp16 alike).
+  if (big >= cu_count && N % 224 == 0) {
+    const int64_t r256 = (big + cu_count - 1) / cu_count;
+    const int64_t r224 = ((int64_t)tiles(M, 256) * (N / 224) + cu_count - 1) / cu_count;
+    if (7 * r224 < 8 * r256) return r224 >= 2 ? CFG_256x224_S2_R128_PERSIST : CFG_256x224_S2_R128;
+  }
   // two or more full rounds of 256 x 256 tiles: the persistent grid, whose
   // workgroups load a tile's first stage while they store the previous
   // tile's C (8192^3: int8 +3.0%, fp16 +1.6%); int4 stays on configuration
@@ -200,8 +216,8 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
   if (mid >= cu_count / 2)
     return kind == KIND_F16 ? CFG_128_S4_R128 : (kind == KIND_I4 ? CFG_128_S2_R256_W4 : CFG_128_S2_R256);
-  // fewer 64 x 64 tiles than half the CUs: 32 x 32 tiles whose eight waves
-  // split K, four times the workgroups (graph-timed, one MI355X: int8 512^3
+  // at most half as many 64 x 64 tiles as CUs: 32 x 32 tiles whose eight
+  // waves split K, four times the workgroups (graph-timed, one MI355X: int8 512^3
   // 2.89 against 3.53 us, int4 2.87 against 3.79, fp16 3.43 against 4.70;
   // int8 512 x 512 x 16384 21.7 against 63.8 us; 768^3, with 144 tiles,
   // stays faster on 64 x 64: 4.23 against 5.26 us)

@@ -1,24 +1,31 @@
 // Tiled MFMA GEMM kernels for gfx950 (CDNA4).
 //
-// One template serves the four entry points.  A workgroup computes a BM x BN
-// tile of C.  Both operands are K-contiguous, so a K-stage of a tile is a
-// block of rows of 128 LDS bytes each (128 int8, 64 fp16, or 128 int4 values
-// once unpacked to int8):
+// Template families serve the entry points; each workgroup computes a tile
+// of C.  Both operands are K-contiguous (one gemm_v3 variant also takes B as
+// K x N), so a K-stage of a tile is a block of operand rows:
 //
-//   global  --16-byte buffer loads (out-of-range reads return 0)-->  VGPRs
-//   VGPRs   --ds_write_b128, XOR-swizzled 16-byte chunks-->          LDS stage
-//   LDS     --ds_read_b128 fragments-->                              MFMA 32x32
-//
-// Two LDS stages: while the waves contract stage s, the next K-stage is
-// already in flight from global memory into registers, and is written to the
-// other stage after the MFMAs; one barrier per K-stage separates the phases.
+//   gemm_v3 (the default above a few hundred rows): 16-byte direct-to-LDS
+//     buffer loads put each stage's rows straight into an XOR-swizzled LDS
+//     ring (2-8 stages), ds_read_b128 fragments feed 32x32 MFMAs, and one
+//     barrier per stage rotates the ring.  Knobs select the tile, the ring,
+//     the load schedule, the C stores, a persistent grid that walks its
+//     tiles round by round, and split-K over a caller's workspace.
+//   gemm_tiled (the first kernel, kept for small grids): loads into VGPRs,
+//     ds_write_b128 into LDS, then the same fragment reads.
+//   gemm_skinny* (short M, and small products): the waves of a workgroup
+//     split K, B goes through LDS, and the partial sums meet in LDS.
+//   gemm_ref: one unswizzled stage, nothing pipelined, the depth-1
+//     reference the tuned kernels are checked against.
+//   gemm_pingpong, gemm_stream: measured alternatives (two wave groups
+//     alternating memory and MFMA phases; a loader wave with a deep B ring).
 //
 // The pages' kernels (the PTX-vs-WMMA summary page; the async Tensor Core
 // article, sections on the synchronous data path, cp.async, multi-stage
 // buffering and swizzle) move tiles global -> shared -> registers -> mma with
 // cp.async pipelining and swizzled shared memory.  On CDNA4 the MFMA reads its
 // operands from VGPRs, so the same three-level path is built from buffer
-// loads, LDS and ds_read_b128; there is no TMA or mbarrier to port.
+// loads (direct to LDS), LDS and ds_read_b128; there is no TMA or mbarrier to
+// port.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -509,7 +516,11 @@ struct Acc_elem4 {
 // owns a (BM/2) x (BN/2) quadrant made of 32 x 32 MFMA blocks, so that at
 // BM = BN = 256 every wave keeps 16 independent accumulator chains in flight
 // (a 32 x 32 MFMA needs about 8 per SIMD to run at full rate) and reads half
-// as many LDS bytes per MAC as an 8-wave 128 x 64 split.
+// as many LDS bytes per MAC as an 8-wave 128 x 64 split.  A tile 224
+// columns wide (seven 32-column blocks, for N a multiple of 224 such as
+// 14336) cannot be halved into 32-column blocks, so there each wave owns a
+// band of BM/4 rows by all 224 columns (2 x 7 blocks, 14 chains); its
+// epilogue stores a 224-column row with 56 lanes and leaves 8 idle.
 //
 // Operand rows stay K-contiguous in LDS, ROWB (64 or 128) bytes per row per
 // K-stage: int8 or fp16 values, or packed int4 (int4 stays packed in LDS and
@@ -665,9 +676,13 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   // int4 with pinned loads expands a K-step's operands once, ahead of the
   // pinned MFMAs, so that they are not rebuilt between scheduling barriers
   constexpr bool kOnce = HIL && I4;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  // wave layout: 2 x 2 quadrants, or, for tiles whose width is an odd
+  // multiple of 32 columns (224: N = 64 x 224 = 14336), four row bands of
+  // the full width
+  constexpr int kWavesN = BN % 64 == 0 ? 2 : 1;
+  constexpr int WTM = BM / (4 / kWavesN), WTN = BN / kWavesN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  static_assert(TM % 2 == 0 && TN >= 1 && BM % 128 == 0 && BN % 64 == 0, "tile");
+  static_assert(TM % 2 == 0 && TN >= 1 && BM % 128 == 0 && BN % 32 == 0, "tile");
   constexpr int kRows = BM + BN;
   constexpr int kStage = kRows * ROWB;
   constexpr int kRowsPerLoad = 1024 / ROWB;          // rows one 1 KiB wave load fills
@@ -677,10 +692,10 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   constexpr int kSlotsA = BM / kRowsPerLoad / 4;
   static_assert((STAGES - 2) * kSlots <= 63, "vmcnt range");
   constexpr int kMainLds = STAGES * kStage;
-  // epilogue staging: per wave 64 rows (32 when persistent) of WTN 4-byte
-  // values plus 32 B padding
+  // epilogue staging: per wave 64 rows (32 when persistent; half as many for
+  // 224-column rows) of WTN 4-byte values plus 32 B padding
   constexpr int kEpiPitch = WTN * 4 + 32;
-  constexpr int kEpiRows = PERSIST ? 32 : 64;
+  constexpr int kEpiRows = (PERSIST ? 32 : 64) / (WTN > 128 ? 2 : 1);
   constexpr int kEpiWave = kEpiRows * kEpiPitch;
   constexpr int kEpiLds = 4 * kEpiWave;
   static_assert(!PERSIST || (STAGES == 2 && !PF && !BKN && !SPLIT && KIND != KIND_I8_MOD), "persistent variant");
@@ -704,7 +719,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
 
   // this workgroup's (first) tile; persistent: round r takes logical tile
   // r G + xcd_logical(workgroup)
@@ -1234,9 +1249,13 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     uint8_t* stage_out = smem + stage_off;
     const int row0 = m0 + wm * WTM;
     const int col0 = n0 + wn * WTN;
-    // each lane stores 16 bytes; lanes 0..WTN/4-1 cover one row
+    // each lane stores 16 bytes; lanes 0..WTN/4-1 cover one row (a row of
+    // 224 columns: lanes 0-55 store, 56-63 read row 0 and store nothing)
     constexpr int kLanesPerRow = WTN / 4;
     constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    constexpr bool kAllLanes = 64 % kLanesPerRow == 0;
+    const bool lane_on = kAllLanes || lane < kRowsPerStore * kLanesPerRow;
+    const int lane_row = lane_on ? lane / kLanesPerRow : 0;
     const int c_lane = (lane % kLanesPerRow) * 4;
     // dequant: the column scales of this lane's four output columns (the
     // same in every row it stores; zero outside C)
@@ -1246,26 +1265,27 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
       for (int x = 0; x < 4; ++x)
         if (col0 + c_lane + x < p.N) cs4[x] = p.col_scale[col0 + c_lane + x];
     }
-    constexpr int kBlk = kEpiRows / 32;   // accumulator block rows per pass
+    static_assert(WTM % kEpiRows == 0 && kEpiRows % 8 == 0, "epilogue passes");
 #pragma unroll
-    for (int half = 0; half < TM / kBlk; ++half) {
-      // accumulator blocks i = kBlk*half .. + kBlk - 1 cover kEpiRows rows of
-      // the quadrant
+    for (int half = 0; half < WTM / kEpiRows; ++half) {
+      // pass `half` stages the wave's rows half*kEpiRows .. + kEpiRows - 1:
+      // the accumulator elements whose 8-row group (block i, element e / 4)
+      // falls there
 #pragma unroll
-      for (int ii = 0; ii < kBlk; ++ii) {
-        const int i = kBlk * half + ii;
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int r = ii * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+            const int rg = i * 32 + 8 * (e >> 2);
+            if (rg / kEpiRows != half) continue;
+            const int r = rg - half * kEpiRows + 4 * fh + (e & 3);
             const int c = j * 32 + fr;
             // dequant: the raw sums go through LDS; the scales are applied
             // as the rows are stored
             *(uint32_t*)(stage_out + r * kEpiPitch + c * 4) =
                 KIND == KIND_I8_DEQUANT ? (uint32_t)acc[i][j][e] : value(i, j, e);
           }
-      }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes done
       // dequant: lane l holds the scale of row l of these kEpiRows (zero
       // outside C); each store's rows take theirs by lane index
@@ -1289,7 +1309,7 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
           for (int q = 0; q < kRowsPerStore; ++q) {
             const float sq = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rs_half), r0 + q));
-            if (lane / kLanesPerRow == q) rs = sq;
+            if (lane_row == q) rs = sq;
           }
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
@@ -1305,11 +1325,12 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
         // int4: one row at a time (its main loop already holds 256 VGPRs)
 #pragma unroll
         for (int r0 = 0; r0 < kEpiRows; r0 += kRowsPerStore) {
-          const int r = r0 + lane / kLanesPerRow;
+          const int r = r0 + lane_row;
           i32x4 v = *(const i32x4*)(stage_out + r * kEpiPitch + c_lane * 4);
           const int grow = row0 + half * kEpiRows + r;
           uint32_t* dst = (uint32_t*)p.C + (size_t)grow * p.N + gcol;
-          if (full) {
+          if (!lane_on) {
+          } else if (full) {
             if constexpr (NTC) __builtin_nontemporal_store(v, (i32x4*)dst);
             else *(i32x4*)dst = v;
           } else if (grow < p.M) {
@@ -1324,27 +1345,29 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
           i32x4 v[kGroup];
 #pragma unroll
           for (int q = 0; q < kGroup; ++q) {
-            const int r = (g + q) * kRowsPerStore + lane / kLanesPerRow;
+            const int r = (g + q) * kRowsPerStore + lane_row;
             v[q] = *(const i32x4*)(stage_out + r * kEpiPitch + c_lane * 4);
           }
 #pragma unroll
           for (int q = 0; q < kGroup; ++q) {
             const int r0 = (g + q) * kRowsPerStore;
             const i32x4 w = scaled(v[q], r0);
-            const int grow = row0 + half * kEpiRows + r0 + lane / kLanesPerRow;
+            const int grow = row0 + half * kEpiRows + r0 + lane_row;
             i32x4* dst = (i32x4*)((uint32_t*)p.C + (size_t)grow * p.N + gcol);
-            if constexpr (NTC) __builtin_nontemporal_store(w, dst);
-            else *dst = w;
+            if (lane_on) {
+              if constexpr (NTC) __builtin_nontemporal_store(w, dst);
+              else *dst = w;
+            }
           }
         }
       } else {
 #pragma unroll
         for (int r0 = 0; r0 < kEpiRows; r0 += kRowsPerStore) {
-          const int r = r0 + lane / kLanesPerRow;
+          const int r = r0 + lane_row;
           const i32x4 v = scaled(*(const i32x4*)(stage_out + r * kEpiPitch + c_lane * 4), r0);
           const int grow = row0 + half * kEpiRows + r;
           uint32_t* dst = (uint32_t*)p.C + (size_t)grow * p.N + gcol;
-          if (grow < p.M) {
+          if (lane_on && grow < p.M) {
 #pragma unroll
             for (int x = 0; x < 4; ++x)
               if (gcol + x < p.N) dst[x] = (uint32_t)v[x];

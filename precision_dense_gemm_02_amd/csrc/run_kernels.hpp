@@ -106,6 +106,19 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
           stream);
     case CFG_128_S4_R128:
       return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
+    case CFG_256x224_S2_R128:
+      return launch<256, 224>(
+          (const void*)&gemm_v3<KIND, 256, 224, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads>, args, 256,
+          stream);
+    case CFG_256x224_S2_R128_PERSIST:
+      if constexpr (KIND == KIND_I4)
+        return launch<256, 224>(
+            (const void*)&gemm_v3<KIND, 256, 224, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads>, args, 256,
+            stream);
+      else
+        return launch_persistent<256, 224>(
+            (const void*)&gemm_v3<KIND, 256, 224, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads, true>,
+            args, 256, stream, dev.cu_count);
     case CFG_256_S2_R128_PERSIST:
       // int4 keeps configuration 0: its kernel already holds 256 VGPRs, and
       // the persistent variant's extra state would spill

@@ -26,7 +26,11 @@ DEFAULT_KERNELS = {
     "lpgemm::gemm_v3<1, 256, 256, 2, 128, 0, false, false, 2, false, 0, false, false, false, 0, false, false>": "int4, >= 1 round of 256x256 tiles",
     "lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false, false>": "fp16, >= 2 rounds (8192^3), persistent",
     "lpgemm::gemm_v3<2, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false, 0, false, false>": "fp16, 1-2 rounds (4096^3)",
-    "lpgemm::gemm_v3<3, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false, 0, false, false>": "dequant int8 (LLM M = 2048)",
+    "lpgemm::gemm_v3<3, 256, 256, 2, 128, 0, false, false, 2, true, 0, false, true, false, 0, false, false>": "dequant int8, 1-2 rounds of 256x256 tiles",
+    "lpgemm::gemm_v3<0, 256, 224, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false, false>": "int8, N a multiple of 224 (N = 14336), >= 2 rounds of 256x224 tiles, persistent",
+    "lpgemm::gemm_v3<2, 256, 224, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false, false>": "fp16, N a multiple of 224, persistent",
+    "lpgemm::gemm_v3<3, 256, 224, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false, false>": "dequant int8, N a multiple of 224 (LLM M = 2048), persistent",
+    "lpgemm::gemm_v3<1, 256, 224, 2, 128, 0, false, false, 2, false, 0, false, false, false, 0, false, false>": "int4, N a multiple of 224",
     "lpgemm::gemm_v3<0, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "int8, 128x128 tiles (2048^3)",
     "lpgemm::gemm_v3<2, 128, 128, 4, 128, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "fp16, 128x128 tiles (2048^3)",
     "lpgemm::gemm_v3<1, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 1, false, false>": "int4, 128x128 tiles (2048^3), 32-byte fragment reads",

@@ -127,16 +127,19 @@ def test_skinny_long_k(forced, M):
 # the persistent configuration walks several tiles per workgroup: shapes
 # with more 256 x 256 tiles than a 256-CU device has workgroups, ragged
 # edges, and stage counts of both parities (the LDS stage holding a tile's
-# first K-stage then alternates from tile to tile)
+# first K-stage then alternates from tile to tile); configuration 62 is the
+# same grid over 256 x 224 tiles, whose epilogue stages 16 rows per wave
 PERSIST_CFG = 47
+PERSIST_CFGS = [PERSIST_CFG, 62]
 
 
+@pytest.mark.parametrize("cfg", PERSIST_CFGS)
 @pytest.mark.parametrize("M,N,K", [(4100, 4100, 16), (4100, 4100, 272), (4100, 4100, 400),
-                                   (8192, 4160, 1040), (8192, 8192, 128)])
-def test_persistent_i8_rounds(M, N, K):
-    print("[case] persistent i8", M, N, K, flush=True)
+                                   (8192, 4160, 1040), (8192, 8192, 128), (4100, 14336, 272)])
+def test_persistent_i8_rounds(M, N, K, cfg):
+    print("[case] persistent i8", cfg, M, N, K, flush=True)
     p = inputs.int8_problem(M, N, K, seed=M + N + K)
-    prev = lp.force_config(PERSIST_CFG)
+    prev = lp.force_config(cfg)
     try:
         out = lp.gemm_i8(_dev(p.a), _dev(p.b_t), out=torch.full((M, N), -7, dtype=torch.int32, device="cuda"))
         torch.cuda.synchronize()
@@ -164,12 +167,13 @@ def test_persistent_i4_rounds(K, cfg):
     np.testing.assert_array_equal(out.cpu().numpy()[rows], oracle.gemm_i4(p.a_packed, p.b_packed, K, rows=rows))
 
 
+@pytest.mark.parametrize("cfg", PERSIST_CFGS)
 @pytest.mark.parametrize("K", [8, 136, 200])
-def test_persistent_f16_rounds(K):
+def test_persistent_f16_rounds(K, cfg):
     M, N = 4100, 4100
-    print("[case] persistent f16", M, N, K, flush=True)
+    print("[case] persistent f16", cfg, M, N, K, flush=True)
     p = inputs.f16_integer_problem(M, N, K, seed=K)
-    prev = lp.force_config(PERSIST_CFG)
+    prev = lp.force_config(cfg)
     try:
         out = lp.gemm_f16(_dev(p.a), _dev(p.b_t))
         torch.cuda.synchronize()
@@ -180,11 +184,13 @@ def test_persistent_f16_rounds(K):
     np.testing.assert_array_equal(out.cpu().numpy()[rows], ref.astype(np.float32))
 
 
-def test_persistent_dequant_llm_2048():
-    # the LLM projection at M = 2048: 448 tiles, a full round and a partial one
-    print("[case] persistent dequant llm 2048", flush=True)
+@pytest.mark.parametrize("cfg", PERSIST_CFGS)
+def test_persistent_dequant_llm_2048(cfg):
+    # the LLM projection at M = 2048: 448 tiles of 256 x 256, a full round and
+    # a partial one; 512 tiles of 256 x 224, two full rounds
+    print("[case] persistent dequant llm 2048", cfg, flush=True)
     p = inputs.llm_problem(2048)
-    prev = lp.force_config(PERSIST_CFG)
+    prev = lp.force_config(cfg)
     try:
         out = lp.gemm_i8_dequant(_dev(p.a), _dev(p.b_t), _dev(p.row_scale), _dev(p.col_scale))
         torch.cuda.synchronize()

@@ -85,3 +85,38 @@ def test_int_kinds_reference_equals_oracle():
     np.testing.assert_array_equal(cd.cpu().numpy().view(np.uint32),
                                   oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale).view(np.uint32))
     np.testing.assert_array_equal(c4.cpu().numpy(), oracle.gemm_i4(q.a_packed, q.b_packed, 416))
+
+
+@pytest.mark.parametrize("kind", ["i8", "i4", "f16", "dq"])
+def test_llm_projection_2048_equals_reference(kind):
+    # M = 2048, N = 14336 = 64 x 224, K = 4096: the automatic choice takes
+    # 256 x 224 tiles (configuration 61, four waves of 64 x 224, an epilogue
+    # whose 56 lanes per row leave 8 idle), full C against the reference
+    M, N, K = 2048, 14336, 4096
+    print("[case] reference, LLM projection", kind, M, N, K, flush=True)
+    if kind == "f16":
+        p = inputs.f16_problem(M, N, K, seed=61)
+        args = (torch.from_numpy(p.a).cuda(), torch.from_numpy(p.b_t).cuda())
+        fn = lp.gemm_f16
+    elif kind == "i4":
+        p = inputs.int4_problem(M, N, K, seed=61)
+        args = (torch.from_numpy(p.a_packed).cuda(), torch.from_numpy(p.b_packed).cuda(), K)
+        fn = lp.gemm_i4
+    else:
+        p = inputs.llm_problem(M)
+        args = (torch.from_numpy(p.a).cuda(), torch.from_numpy(p.b_t).cuda())
+        fn = lp.gemm_i8
+        if kind == "dq":
+            args += (torch.from_numpy(p.row_scale).cuda(), torch.from_numpy(p.col_scale).cuda())
+            fn = lp.gemm_i8_dequant
+    ref = _run(REF, fn, *args)
+    for cfg in (61, 62):   # 62: the persistent grid over the same tiles
+        forced = _run(cfg, fn, *args)
+        assert torch.equal(forced.view(torch.int32), ref.view(torch.int32)), f"configuration {cfg}"
+    got = fn(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    if kind == "dq":
+        rows = [0, 1, 255, 256, 1023, M - 1]
+        want = oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale, rows=rows)
+        np.testing.assert_array_equal(got.cpu().numpy()[rows].view(np.uint32), want.view(np.uint32))

@@ -138,7 +138,8 @@ enum KernelCfg {
   CFG_128_S2_R256_SPLITK = 60,   // configuration 36 (int4: 48) with K split over workgroups (needs a workspace)
   CFG_256x224_S2_R128 = 61,      // configuration 0 with 256 x 224 tiles (four waves of 64 x 224)
   CFG_256x224_S2_R128_PERSIST = 62,  // configuration 61 as a persistent grid (int4: 61)
-  CFG_COUNT = 63
+  CFG_SKINNY_PIPE_W4R2_N2 = 63,  // configuration 14 with two 32-row B blocks per workgroup (up to 64 columns)
+  CFG_COUNT = 64
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -173,6 +174,27 @@ inline KernelCfg choose_config_e3m2(int64_t M, int64_t N, int cu_count) {
   return CFG_128x64_S6_R128;
 }
 
+// Columns of C per workgroup for the skinny kernel at M <= 32 with `nb`
+// 32-row B blocks per workgroup (configs 14 and 63): a multiple of 4 that
+// spreads the N columns evenly over the workgroups the CUs hold at once
+// (two per CU of one block, one of two blocks) or a few times as many, when
+// that leaves the busiest CU fewer columns than 32-column tiles do; 0
+// otherwise.  At least 24 columns: below that each workgroup's copy of the
+// A rows outweighs its share of B.  N = 14336 on 256 CUs: 28 columns with
+// one block (512 workgroups, 56 columns per CU against two 32-column tiles
+// on 192 CUs); N = 8192 and 16384 already spread evenly.
+inline int skinny_columns(int64_t N, int cu_count, int nb) {
+  if (cu_count <= 0 || N <= 0) return 0;
+  const int per_cu = nb == 1 ? 2 : 1;
+  const int64_t plain = ((int64_t)tiles(N, 32) + cu_count - 1) / cu_count * 32;
+  for (int64_t k = 1; k <= 4; ++k) {
+    const int64_t groups = (int64_t)cu_count * per_cu * k;
+    const int64_t w = ((N + groups - 1) / groups + 3) / 4 * 4;
+    if (w <= 32 * nb) return w >= 24 && per_cu * k * w < plain ? (int)w : 0;
+  }
+  return 0;
+}
+
 inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   const int f = forced_config();
   // configurations 45 and 46 differ from 0 only for the E3M2 kind and for
@@ -180,7 +202,8 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   if (f == CFG_256_S2_R128_PIN_E3M2 || f == CFG_256_S2_R128_PIN_KXN) return CFG_256_S2_R128;
   if (f >= 0) return (KernelCfg)f;
   const bool int8_rows = kind == KIND_I8 || kind == KIND_I8_DEQUANT;
-  // few rows against many columns: stream B with split-K workgroups
+  // few rows against many columns: stream B with split-K workgroups, each
+  // owning an equal share of the columns where that helps (skinny_columns)
   if (M <= 32) return CFG_SKINNY_PIPE_W4R2;
   if (M <= 64) return CFG_SKINNY_64;
   // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128.
@@ -314,6 +337,20 @@ template <int BM, int BN>
 lpgemm_status launch(const void* fn, GemmArgs args, int threads, hipStream_t stream) {
   args.tiles_m = tiles(args.M, BM);
   args.tiles_n = tiles(args.N, BN);
+  args.group_m = 8;
+  const int64_t nblocks = (int64_t)args.tiles_m * args.tiles_n;
+  if (nblocks > INT32_MAX) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;
+  void* kargs[] = {&args};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblocks), dim3(threads), kargs, 0, stream);
+  return e == hipSuccess ? LPGEMM_SUCCESS : LPGEMM_ERROR_LAUNCH;
+}
+
+// A launch of the skinny pipelined kernel with `w` columns per workgroup
+// (at most its 32 NB B rows).
+inline lpgemm_status launch_skinny(const void* fn, GemmArgs args, int threads, hipStream_t stream, int w) {
+  args.tile_w = w;
+  args.tiles_m = tiles(args.M, 32);
+  args.tiles_n = tiles(args.N, w);
   args.group_m = 8;
   const int64_t nblocks = (int64_t)args.tiles_m * args.tiles_n;
   if (nblocks > INT32_MAX) return LPGEMM_ERROR_UNSUPPORTED_SHAPE;

@@ -78,6 +78,9 @@ struct GemmArgs {
   int splits;
   uint32_t* split_count;
   uint32_t* split_part;
+  // gemm_skinny_pipe: columns of C per workgroup (at most its 32 NB B rows;
+  // 0: all of them)
+  int tile_w;
 };
 
 // Position of 16-byte chunk `c` of LDS row `r` within that row.  XOR with a
@@ -1963,11 +1966,12 @@ __device__ __forceinline__ void skinny_block(typename KindTraits<KIND>::Acc (&ac
 template <int KIND, int MT, int NT, int WAVES, int kPitch, int kWaveWords>
 __device__ __forceinline__ void skinny_reduce_store_strided(const GemmArgs& p, const uint32_t* red,
                                                             int m0, int n0,
-                                                            const float* rs_local = nullptr) {
+                                                            const float* rs_local = nullptr,
+                                                            int ncols = NT) {
   for (int idx = threadIdx.x; idx < MT * NT; idx += WAVES * 64) {
     const int rr = idx / NT, cc = idx % NT;
     const int row = m0 + rr, col = n0 + cc;
-    if (row >= p.M || col >= p.N) continue;
+    if (row >= p.M || col >= p.N || cc >= ncols) continue;
     if constexpr (KIND == KIND_F16) {
       float sum = 0.f;
       for (int w = 0; w < WAVES; ++w) sum += __builtin_bit_cast(float, red[w * kWaveWords + rr * kPitch + cc]);
@@ -2096,7 +2100,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_lds(GemmArgs p) {
   constexpr int kBlock = 128;
   constexpr int MT = 32, NT = 32;
   constexpr int kPitch = NT + 1;
-  constexpr int kBlockLds = NT * kBlock;      // 4 KiB: one K-block of the 32 B rows
+  constexpr int kBlockLds = NT * kBlock;      // one K-block of the NT B rows (4 KiB per 32)
   constexpr int kWaveLds = R * kBlockLds;
   static_assert(kWaveLds >= MT * kPitch * 4, "the partial sums reuse the wave's region");
 
@@ -2270,18 +2274,27 @@ __device__ __forceinline__ float wave_max(float v) {
 // equals the separate quantiser followed by the dequantising GEMM bit for
 // bit.  The scan is repeated by every workgroup of a row band (the cost the
 // Day-12 page ascribes to a quantisation prologue inside the GEMM).
-template <int KIND, int WAVES, int R, bool QA = false>
+//
+// NB, p.tile_w: a workgroup holds NB 32-row blocks of B and owns p.tile_w
+// (at most 32 NB) columns of C from column p.tile_w * (its tile column) on;
+// B rows past its columns read as zero without touching memory and their
+// columns are not stored.  Every workgroup then streams the same number of
+// B rows, so a column width that divides N into as many workgroups as
+// there are CUs (N = 14336 on 256 CUs: 56 columns, NB = 2) loads every CU
+// equally, where 32-column tiles (448) give some CUs two and others one.
+template <int KIND, int WAVES, int R, bool QA = false, int NB = 1>
 __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   static_assert(!QA || KIND == KIND_I8_DEQUANT, "on-the-fly quantisation feeds the dequantising product");
+  static_assert(NB == 1 || NB == 2, "B blocks per workgroup");
   constexpr int kBlock = 128;
-  constexpr int MT = 32, NT = 32;
+  constexpr int MT = 32, NT = 32 * NB;
   constexpr int kPitch = NT + 1;
-  constexpr int kBlockLds = NT * kBlock;      // 4 KiB: one K-block of the 32 B rows
+  constexpr int kBlockLds = NT * kBlock;      // one K-block of the NT B rows (4 KiB per 32)
   constexpr int kRoundLds = R * kBlockLds;
   constexpr int kWaveLds = 2 * kRoundLds;
   constexpr int kAParts = QA ? 2 : 1;         // 16-byte loads per A fragment
-  constexpr int kLoadsPerRound = (4 + 4 * kAParts) * R;   // 4 copies + the A fragments per block
+  constexpr int kLoadsPerRound = (4 * NB + 4 * kAParts) * R;   // 4 NB copies + the A fragments per block
   static_assert(kWaveLds >= MT * kPitch * 4, "the partial sums reuse the wave's region");
   // two rounds can be outstanding at once; the vector-memory counter holds
   // at most 63, and a wait on a counter that has overflowed passes too early
@@ -2293,9 +2306,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tm = blockIdx.x / p.tiles_n, tn = blockIdx.x % p.tiles_n;
-  const int m0 = tm * MT, n0 = tn * NT;
+  const int tile_w = p.tile_w > 0 ? p.tile_w : NT;
+  const int m0 = tm * MT, n0 = tn * tile_w;
   const int rows_a = min(MT, p.M - m0);
-  const int rows_b = min(NT, p.N - n0);
+  const int rows_b = min(tile_w, p.N - n0);
   // bytes per row of A: K (int8) or 2K (binary16)
   const uint32_t a_stride = (uint32_t)p.row_bytes * kAParts;
   const i32x4 rsrc_a = make_rsrc(p.A + (size_t)m0 * a_stride, rows_a * a_stride);
@@ -2331,9 +2345,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   const int b1 = (int)(((long long)nblk * (wave + 1)) / WAVES);
   const int rounds = (b1 - b0 + R - 1) / R;
 
-  uint32_t dma_off[4], dma_col[4];
+  uint32_t dma_off[4 * NB], dma_col[4 * NB];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < 4 * NB; ++t) {
     const int row = 8 * t + (lane >> 3);
     const int c = swizzle_chunk(row, lane & 7);
     dma_off[t] = (uint32_t)row * row_bytes + c * 16;
@@ -2344,11 +2358,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) frag_off[q] = r * kBlock + (swizzle_chunk(r, 4 * h + q) << 4);
 
-  Acc acc[R][1];
+  Acc acc[R][NB][1];
 #pragma unroll
   for (int j = 0; j < R; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[j][0][e] = 0;
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][nb][0][e] = 0;
 
   i32x4 fa[2][R][1][4 * kAParts];
 
@@ -2370,7 +2386,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
                         ok ? a_row + kAParts * col + 16 * part : kOutOfRange);
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 4 * NB; ++t) {
         const bool ok = in_range && kbyte + dma_col[t] < row_bytes;
         lds_dma_16(rsrc_b, my_lds + buf * kRoundLds + j * kBlockLds + t * 1024,
                    ok ? dma_off[t] + kbyte : kOutOfRange);
@@ -2388,14 +2404,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
     } else {
       wait_vmcnt<0>();
     }
-    i32x4 fb[R][4];
+    i32x4 fb[R][NB][4];
 #pragma unroll
     for (int j = 0; j < R; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
 #pragma unroll
         for (int part = 0; part < kAParts; ++part) pin_after_wait(fa[buf][j][0][kAParts * q + part]);
-        fb[j][q] = *(const i32x4*)(my_smem + buf * kRoundLds + j * kBlockLds + frag_off[q]);
+        // block nb's rows start 32 rows on, which leaves the swizzle unchanged
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          fb[j][nb][q] = *(const i32x4*)(my_smem + buf * kRoundLds + j * kBlockLds + nb * 32 * kBlock + frag_off[q]);
       }
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -2408,9 +2427,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
           const uint64_t hi = qs != 0.f ? quantize8(__builtin_bit_cast(f16x8, fa[buf][j][0][2 * q + 1]), qs, qr) : 0;
           qa[0][q] = i32x4{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
         }
-        skinny_block<KIND, 1>(acc[j], qa, fb[j]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) skinny_block<KIND, 1>(acc[j][nb], qa, fb[j][nb]);
       } else {
-        skinny_block<KIND, 1>(acc[j], fa[buf][j], fb[j]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) skinny_block<KIND, 1>(acc[j][nb], fa[buf][j], fb[j][nb]);
       }
     }
   };
@@ -2423,13 +2444,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
 #pragma unroll
   for (int j = 1; j < R; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[0][0][e] += acc[j][0][e];
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[0][nb][0][e] += acc[j][nb][0][e];
 
   wait_lgkmcnt0();
-  skinny_store_partials<KIND, 1, kPitch>(acc[0], (uint32_t*)my_smem, lane);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    skinny_store_partials<KIND, 1, kPitch>(acc[0][nb], (uint32_t*)my_smem + 32 * nb, lane);
   __syncthreads();
   skinny_reduce_store_strided<KIND, MT, NT, WAVES, kPitch, kWaveLds / 4>(p, (const uint32_t*)smem, m0, n0,
-                                                                          QA ? row_s : nullptr);
+                                                                          QA ? row_s : nullptr, tile_w);
 }
 
 }  // namespace lpgemm

@@ -201,15 +201,16 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   // K x N B
   if (f == CFG_256_S2_R128_PIN_E3M2 || f == CFG_256_S2_R128_PIN_KXN) return CFG_256_S2_R128;
   if (f >= 0) return (KernelCfg)f;
-  const bool int8_rows = kind == KIND_I8 || kind == KIND_I8_DEQUANT;
   // few rows against many columns: stream B with split-K workgroups, each
   // owning an equal share of the columns where that helps (skinny_columns)
   if (M <= 32) return CFG_SKINNY_PIPE_W4R2;
   if (M <= 64) return CFG_SKINNY_64;
-  // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128.
-  // int8 rows stream B in 256-byte pieces per stage (M = 128, K = 4096,
-  // N = 14336: 19.2 us against 20.4 us with six 128-byte stages)
-  if (M <= 128) return int8_rows ? CFG_128x64_S3_R256 : CFG_128x64_S6_R128;
+  // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128, and
+  // B streams in 256-byte pieces per stage (graph-timed, one MI355X, against
+  // six 128-byte stages: dequant M = 128, K = 4096, N = 14336 19.2 against
+  // 20.4 us; fp16 there 555 against 524-541 TFLOP/s, fp16 128 x 8192 x 8192
+  // 444 against 364; int4 128 x 14336 x 4096 846 against 804 TOP/s)
+  if (M <= 128) return CFG_128x64_S3_R256;
   const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
   // N a multiple of 224 (the LLM projection's 14336 = 64 x 224): 256 x 224
   // tiles when their rounds of one tile per CU, each 7/8 of a 256 x 256

@@ -204,7 +204,15 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   // few rows against many columns: stream B with split-K workgroups, each
   // owning an equal share of the columns where that helps (skinny_columns)
   if (M <= 32) return CFG_SKINNY_PIPE_W4R2;
-  if (M <= 64) return CFG_SKINNY_64;
+  // 33-64 rows: the 128-row band kernel below once its 64-column tiles
+  // number more than half the CUs, else the skinny kernel over two 32-row
+  // bands; int4 always the skinny kernel (graph-timed at K = 4096, one
+  // MI355X: dequant M = 64, N = 14336 512 TOP/s against 317 skinny and 242
+  // for the earlier choice, the split-K kernel of 64-row tiles; fp16 there
+  // 329 against 176 TFLOP/s; N = 8192 (128 tiles) 317 against 343 skinny;
+  // int4 N = 14336 595 skinny against 423)
+  if (M <= 64)
+    return kind != KIND_I4 && (int64_t)tiles(N, 64) > cu_count / 2 ? CFG_128x64_S3_R256 : CFG_SKINNY_PIPE_W4R2;
   // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128, and
   // B streams in 256-byte pieces per stage (graph-timed, one MI355X, against
   // six 128-byte stages: dequant M = 128, K = 4096, N = 14336 19.2 against

@@ -195,7 +195,7 @@ inline int skinny_columns(int64_t N, int cu_count, int nb) {
   return 0;
 }
 
-inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
+inline KernelCfg choose_config(int64_t M, int64_t N, int64_t K, int cu_count, int kind) {
   const int f = forced_config();
   // configurations 45 and 46 differ from 0 only for the E3M2 kind and for
   // K x N B
@@ -221,33 +221,54 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int cu_count, int kind) {
   if (M <= 128) return CFG_128x64_S3_R256;
   const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
   // N a multiple of 224 (the LLM projection's 14336 = 64 x 224): 256 x 224
-  // tiles when their rounds of one tile per CU, each 7/8 of a 256 x 256
-  // round's work, add up to less (M = 2048: 512 tiles in two full rounds
-  // against 448 in 1.75), on the persistent grid from two rounds on (int4:
-  // the plain grid).  Graph-timed, K = 4096, int8, plain 224 grid: M = 2048
-  // 2173 TOP/s against 2152 with 256 x 256 tiles (1.75 rounds), M = 4096
-  // 2156 against 2064 on the persistent 256 x 256 grid (3.5 rounds), one
-  // MI355X; on another, the persistent 224 grid 2-3.5% ahead of the plain
-  // one at both sizes and at M = 6144 (dequant and fp16 alike).
-  if (big >= cu_count && N % 224 == 0) {
+  // tiles once they fill at least half the CUs and their rounds of one tile
+  // per CU, each 7/8 of a 256 x 256 round's work, add up to less (M = 2048:
+  // 512 tiles in two full rounds against 448 in 1.75), on the persistent
+  // grid from two full rounds on (int4: the plain grid).  Graph-timed,
+  // K = 4096, one MI355X: dequant M = 1024 1959 TOP/s against 1950 with
+  // 256 x 256 tiles and 1329 with 128 x 128; M = 768 1808 against 1752 and
+  // 1332; M = 512 (128 tiles) 1456 against 1404 for 128 x 128 tiles;
+  // M = 1536 (1.5 rounds) 1725 plain against 1568 persistent; int8
+  // M = 4096 2156 against 2064 on the persistent 256 x 256 grid (3.5
+  // rounds); the persistent 224 grid 2-3.5% ahead of the plain one at
+  // M = 2048, 4096, 6144.
+  if (N % 224 == 0) {
+    const int64_t t224 = (int64_t)tiles(M, 256) * (N / 224);
     const int64_t r256 = (big + cu_count - 1) / cu_count;
-    const int64_t r224 = ((int64_t)tiles(M, 256) * (N / 224) + cu_count - 1) / cu_count;
-    if (7 * r224 < 8 * r256) return r224 >= 2 ? CFG_256x224_S2_R128_PERSIST : CFG_256x224_S2_R128;
+    const int64_t r224 = (t224 + cu_count - 1) / cu_count;
+    if (2 * t224 >= cu_count && 7 * r224 < 8 * r256)
+      return t224 >= 2 * (int64_t)cu_count ? CFG_256x224_S2_R128_PERSIST : CFG_256x224_S2_R128;
   }
-  // two or more full rounds of 256 x 256 tiles: the persistent grid, whose
+  // 256 x 256 tiles once they fill more than half the CUs: on this
+  // power-limited board fewer busy CUs run at a higher clock, and the large
+  // tile moves half the bytes per MAC of a 128 x 128 one (graph-timed, one
+  // MI355X: int8 3072^2 x 4096, 144 tiles, 1696 TOP/s against 1367 for the
+  // best 128 x 128 kernel; dequant 512 x 16384 x 4096, 128 tiles, 1495
+  // against 1569).  Two or more full rounds: the persistent grid, whose
   // workgroups load a tile's first stage while they store the previous
   // tile's C (8192^3: int8 +3.0%, fp16 +1.6%); int4 stays on configuration
-  // 0, whose registers leave no room for the persistent state
-  if (big >= 2 * (int64_t)cu_count && kind != KIND_I4) return CFG_256_S2_R128_PERSIST;
-  if (big >= cu_count) return CFG_256_S2_R128;
-  // 128 x 128 tiles: at 2048^3, two 256-byte stages for int8 and int4
-  // (14.5 / 15.0 us against 15.4 / 15.7 us with four 64-byte stages), four
-  // 128-byte stages for fp16 (23.1 against 25.4 us); int4 reads 32 packed
-  // bytes per fragment there, which removes the bank conflicts of 8-byte
-  // reads on 256-byte rows (1290 against 1248 TOP/s)
+  // 0, whose registers leave no room for the persistent state.  Between
+  // one and two rounds the persistent grid lost (LLM M = 2048: 1757 against
+  // 1919 TOP/s).
+  if (2 * big > cu_count) {
+    if (big >= 2 * (int64_t)cu_count && kind != KIND_I4) return CFG_256_S2_R128_PERSIST;
+    return CFG_256_S2_R128;
+  }
+  // 128 x 128 tiles: fp16 four 128-byte stages (2048^3: 23.1 against 25.4
+  // us with four 64-byte stages); int4 two 256-byte stages with 32-byte
+  // fragment reads, which remove the bank conflicts of 8-byte reads on
+  // 256-byte rows (2048^3: 1290 against 1248 TOP/s); int8 and dequant four
+  // 128-byte stages, or two 256-byte stages for one round of tiles at
+  // K <= 2048 (graph-timed, one MI355X: 2048^2 x 4096 1524 against 1430
+  // TOP/s, 1280 x 4096 x 4096 1234 against 1054, 1536 x 4096 x 8192 1582
+  // against 1445, dequant 512 x 14336 x 2048 (448 tiles) 1248 against
+  // 1190; 2048^3 1247 against 1201 the other way)
   const int64_t mid = (int64_t)tiles(M, 128) * tiles(N, 128);
-  if (mid >= cu_count / 2)
-    return kind == KIND_F16 ? CFG_128_S4_R128 : (kind == KIND_I4 ? CFG_128_S2_R256_W4 : CFG_128_S2_R256);
+  if (mid >= cu_count / 2) {
+    if (kind == KIND_F16) return CFG_128_S4_R128;
+    if (kind == KIND_I4) return CFG_128_S2_R256_W4;
+    return mid <= cu_count && K <= 2048 ? CFG_128_S2_R256 : CFG_128_S4_R128;
+  }
   // at most half as many 64 x 64 tiles as CUs: 32 x 32 tiles whose eight
   // waves split K, four times the workgroups (graph-timed, one MI355X: int8 512^3
   // 2.89 against 3.53 us, int4 2.87 against 3.79, fp16 3.43 against 4.70;

@@ -43,7 +43,7 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
 
   KernelCfg cfg = BKN ? choose_config_kxn(M, N, dev.cu_count)
                 : (KIND == KIND_I4_E3M2 || KIND == KIND_I8_MOD) ? choose_config_e3m2(M, N, dev.cu_count)
-                                                                : choose_config(M, N, dev.cu_count, KIND);
+                                                                : choose_config(M, N, K, dev.cu_count, KIND);
   // split-K: on the automatic choice, products with few 128 x 128 tiles and
   // a long K split it when the caller gave a workspace
   constexpr bool kCanSplit = !BKN && KIND != KIND_I4_E3M2 && KIND != KIND_I8_MOD;

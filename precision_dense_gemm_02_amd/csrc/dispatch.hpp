@@ -224,34 +224,38 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int64_t K, int cu_count, in
   // tiles once they fill at least half the CUs and their rounds of one tile
   // per CU, each 7/8 of a 256 x 256 round's work, add up to less (M = 2048:
   // 512 tiles in two full rounds against 448 in 1.75), on the persistent
-  // grid from two full rounds on (int4: the plain grid).  Graph-timed,
+  // grid when they fill two or more whole rounds (int4: the plain grid).  Graph-timed,
   // K = 4096, one MI355X: dequant M = 1024 1959 TOP/s against 1950 with
   // 256 x 256 tiles and 1329 with 128 x 128; M = 768 1808 against 1752 and
   // 1332; M = 512 (128 tiles) 1456 against 1404 for 128 x 128 tiles;
   // M = 1536 (1.5 rounds) 1725 plain against 1568 persistent; int8
   // M = 4096 2156 against 2064 on the persistent 256 x 256 grid (3.5
   // rounds); the persistent 224 grid 2-3.5% ahead of the plain one at
-  // M = 2048, 4096, 6144.
+  // M = 2048, 4096, 5120, 6144 (whole rounds) and 4-8% behind it at
+  // M = 2560 and 3584 (2.5 and 3.5 rounds).
   if (N % 224 == 0) {
     const int64_t t224 = (int64_t)tiles(M, 256) * (N / 224);
     const int64_t r256 = (big + cu_count - 1) / cu_count;
     const int64_t r224 = (t224 + cu_count - 1) / cu_count;
     if (2 * t224 >= cu_count && 7 * r224 < 8 * r256)
-      return t224 >= 2 * (int64_t)cu_count ? CFG_256x224_S2_R128_PERSIST : CFG_256x224_S2_R128;
+      return t224 >= 2 * (int64_t)cu_count && t224 % cu_count == 0 ? CFG_256x224_S2_R128_PERSIST
+                                                                    : CFG_256x224_S2_R128;
   }
   // 256 x 256 tiles once they fill more than half the CUs: on this
   // power-limited board fewer busy CUs run at a higher clock, and the large
   // tile moves half the bytes per MAC of a 128 x 128 one (graph-timed, one
   // MI355X: int8 3072^2 x 4096, 144 tiles, 1696 TOP/s against 1367 for the
   // best 128 x 128 kernel; dequant 512 x 16384 x 4096, 128 tiles, 1495
-  // against 1569).  Two or more full rounds: the persistent grid, whose
+  // against 1569).  Two or more whole rounds: the persistent grid, whose
   // workgroups load a tile's first stage while they store the previous
-  // tile's C (8192^3: int8 +3.0%, fp16 +1.6%); int4 stays on configuration
-  // 0, whose registers leave no room for the persistent state.  Between
-  // one and two rounds the persistent grid lost (LLM M = 2048: 1757 against
-  // 1919 TOP/s).
+  // tile's C (8192^3: int8 +3.0%, fp16 +1.6%; 6144 x 8192 x 4096, three
+  // rounds, +2.8%); int4 stays on configuration 0, whose registers leave no
+  // room for the persistent state.  With a partial last round the plain
+  // grid, whose workgroups start wherever a CU frees up, was ahead (LLM
+  // M = 2048, 1.75 rounds: 1919 against 1757 TOP/s; 5120 x 8192 x 4096, 2.5
+  // rounds: 2041 against 1939; 7168 x 8192 x 4096, 3.5: 2114 against 2065).
   if (2 * big > cu_count) {
-    if (big >= 2 * (int64_t)cu_count && kind != KIND_I4) return CFG_256_S2_R128_PERSIST;
+    if (big >= 2 * (int64_t)cu_count && big % cu_count == 0 && kind != KIND_I4) return CFG_256_S2_R128_PERSIST;
     return CFG_256_S2_R128;
   }
   // 128 x 128 tiles: fp16 four 128-byte stages (2048^3: 23.1 against 25.4

@@ -258,6 +258,17 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int64_t K, int cu_count, in
     if (big >= 2 * (int64_t)cu_count && big % cu_count == 0 && kind != KIND_I4) return CFG_256_S2_R128_PERSIST;
     return CFG_256_S2_R128;
   }
+  // 128 x 64 tiles with three 256-byte stages (the 128-row band kernel)
+  // when they make between a quarter of a round and one round, at K >=
+  // 2048, except for int4 (graph-timed, one MI355X, against the earlier
+  // 128 x 128 or 64 x 64 choice: int8 1024 x 1024 x 8192 798 against 506
+  // TOP/s, 1024 x 2048 x 2048 956 against 889, 512 x 4096 x 4096 1168
+  // against 1012, 256 x 8192 x 4096 1138 against 1019, 768 x 768 x 4096 401
+  // against 379; fp16 1024 x 1024 x 4096 396 against 253 TFLOP/s; dequant
+  // 256 x 4096 x 4096 672 against 604; at 1024^3 it lost, 382 against 404,
+  // and at 1536^3, 288 tiles, 567 against 784)
+  const int64_t t_band = (int64_t)tiles(M, 128) * tiles(N, 64);
+  if (kind != KIND_I4 && K >= 2048 && 4 * t_band >= cu_count && t_band <= cu_count) return CFG_128x64_S3_R256;
   // 128 x 128 tiles: fp16 four 128-byte stages (2048^3: 23.1 against 25.4
   // us with four 64-byte stages); int4 two 256-byte stages with 32-byte
   // fragment reads, which remove the bank conflicts of 8-byte reads on

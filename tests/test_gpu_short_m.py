@@ -2,7 +2,8 @@
 33-64 rows take the 128-row band kernel (128 x 64 tiles, three 256-byte
 stages) once its tiles number more than half the CUs and the skinny kernel
 over two 32-row bands otherwise (int4: always the skinny kernel); 65-128
-rows the band kernel for every kind.  Integer kinds bit for bit, fp16 on
+rows the band kernel for every kind, and so do small grids above 128 rows
+(below).  Integer kinds bit for bit, fp16 on
 integer-valued operands (exact in fp32) and on random ones within the
 bound; C is filled beforehand so that an unwritten element shows."""
 import numpy as np
@@ -69,3 +70,30 @@ def test_f16(M, N):
     torch.cuda.synchronize()
     ref, den = oracle.gemm_f16(r.a, r.b_t)
     assert oracle.f16_rel_error(out.cpu().numpy(), ref, den)["max_rel"] <= 1e-3
+
+
+# Above 128 rows, grids of 128 x 64 tiles between a quarter of a round and
+# one round at K >= 2048 take the band kernel too (on 256 CUs: 768 x 768,
+# 72 tiles; 300 x 4100, 195 tiles, ragged on both sides; 1024 x 1024 x
+# 8192, 128 tiles, compared on sampled rows)
+@pytest.mark.parametrize("M,N,K2", [(768, 768, 4096), (300, 4100, 2064), (1024, 1024, 8192)])
+def test_band_tiles_small_grids(M, N, K2):
+    print("[case] band tiles, small grid", M, N, K2, flush=True)
+    rows = None if M * N * K2 < 4e9 else sorted({0, 1, 127, 128, 511, 512, M - 1} | set(range(3, M, 97)))
+    p = inputs.int8_problem(M, N, K2, seed=M + N + K2, scales=True)
+    out = lp.gemm_i8(_dev(p.a), _dev(p.b_t), out=torch.full((M, N), -7, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got if rows is None else got[rows], oracle.gemm_i8(p.a, p.b_t, rows=rows))
+    out = lp.gemm_i8_dequant(_dev(p.a), _dev(p.b_t), _dev(p.row_scale), _dev(p.col_scale),
+                             out=torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale, rows=rows)
+    np.testing.assert_array_equal((got if rows is None else got[rows]).view(np.uint32), ref.view(np.uint32))
+    q = inputs.f16_integer_problem(M, N, K2, seed=M + N + K2 + 1)
+    out = lp.gemm_f16(_dev(q.a), _dev(q.b_t), out=torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = oracle.gemm_i8(q.a.astype(np.int8), q.b_t.astype(np.int8), rows=rows).astype(np.float32)
+    np.testing.assert_array_equal(got if rows is None else got[rows], ref)

@@ -203,7 +203,9 @@ lpgemm_status lpgemm_i8_dequant(int64_t M, int64_t N, int64_t K, const int8_t *A
  * its 64 x 64 tiles number more than a quarter of them (below that the
  * unsplit kernel already splits K inside each workgroup), and each operand
  * row holds more than 31 x 256 bytes (int8 K >= 7952, fp16 K >= 3976, int4
- * K >= 15904).  The K dimension of each tile is then split
+ * K >= 15904); below 64 x 256 bytes only when the product's 128 x 64 tiles
+ * number less than half the compute units or the kind is int4 (otherwise
+ * the unsplit kernel was as fast).  The K dimension of each tile is then split
  * over 4 workgroups; each writes its partial sums to the workspace and the
  * last of a tile to finish adds them and writes C.
  * The integer results are exact and equal to the unsplit entry point's bit

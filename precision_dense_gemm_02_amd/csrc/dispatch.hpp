@@ -302,13 +302,19 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int64_t K, int cu_count, in
 // arrival counter, the parts read back) costs a few microseconds per tile,
 // so the automatic choice splits only products whose 128 x 128 tiles fill
 // at most a quarter of the CUs (see splitk_auto_shape), four ways, and only
-// when K spans at least 32 K-stages of 256 bytes (8 per part).  Measured
-// (graph replay, one MI355X): int8 512 x 2048 x 32768 2.5 times, 256 x 4096
-// x 16384 2.0 times, 1024 x 1024 x 8192 1.5 times as fast as the 64 x 64
-// kernel; fp16 1024 x 1024 x 8192 1.9 times; int4 1024 x 1024 x 16384 2.3
-// times.  Two parts of 8 stages lost: int8 1024 x 1024 x 4096 16.4 against
-// 12.8 us, the LLM projection at M = 128, K = 4096 (112 tiles) 23 against
-// 18 us.
+// when K spans at least 32 K-stages of 256 bytes (8 per part); below 64
+// stages only where the unsplit choice, the band kernel's 128 x 64 tiles,
+// fills less than half the CUs, or for int4, which keeps 64 x 64 tiles.
+// Measured (graph replay, one MI355X) against the unsplit choice: int8
+// 512 x 2048 x 32768 1486 against 938 TOP/s, 256 x 4096 x 16384 1163
+// against 891, 1024 x 1024 x 16384 1088 against 877, 600 x 1000 x 8208 (80
+// band tiles) 458 against 405; fp16 1024 x 1024 x 8192 (64 stages of 256
+// bytes) 543 against 442 TFLOP/s; int4 1024 x 1024 x 16384 1276 against
+// 576; unsplit as fast or faster at 32 stages with 128 band tiles: int8
+// 1024 x 1024 x 8192 797 against 775, dequant 256 x 4096 x 8192 775
+// against 794.  Two parts of 8 stages lost: int8 1024 x 1024 x 4096 16.4
+// against 12.8 us, the LLM projection at M = 128, K = 4096 (112 tiles) 23
+// against 18 us.
 //
 // Workspace layout, the same for every shape so that one workspace serves
 // products of any size in turn: 4 KiB of 32-bit arrival counters (tile t
@@ -340,20 +346,24 @@ inline bool splitk_auto_shape(int64_t M, int64_t N, int cu_count) {
 }
 
 // Parts for the automatic choice with `nks` 256-byte K-stages (1: no split).
-inline int splitk_auto_splits(int64_t M, int64_t N, int nks, int cu_count) {
-  if (!splitk_auto_shape(M, N, cu_count)) return 1;
-  return nks >= kMaxSplits * kMinStagesPerSplit ? kMaxSplits : 1;
+inline int splitk_auto_splits(int64_t M, int64_t N, int nks, int cu_count, int kind) {
+  if (!splitk_auto_shape(M, N, cu_count) || nks < kMaxSplits * kMinStagesPerSplit) return 1;
+  if (nks < 2 * kMaxSplits * kMinStagesPerSplit && kind != KIND_I4 &&
+      2 * (int64_t)tiles(M, 128) * tiles(N, 64) >= cu_count)
+    return 1;
+  return kMaxSplits;
 }
 
 // Parts for a launch of configuration 60 with `nks` K-stages and a
 // workspace of `ws_bytes`: the automatic count (when forced: at least 2,
 // at most one part per K-stage and as many as fill the CUs once), and 1 when
 // the workspace is missing or too small.
-inline int splitk_launch_splits(int64_t M, int64_t N, int nks, int cu_count, const void* ws, int64_t ws_bytes) {
+inline int splitk_launch_splits(int64_t M, int64_t N, int nks, int cu_count, int kind, const void* ws,
+                                int64_t ws_bytes) {
   if (!ws) return 1;
   const int64_t t = (int64_t)tiles(M, kSplitTile) * tiles(N, kSplitTile);
   if (t > kMaxSplitTiles) return 1;
-  int s = splitk_auto_splits(M, N, nks, cu_count);
+  int s = splitk_auto_splits(M, N, nks, cu_count, kind);
   if (s < 2) {
     const int64_t fill = cu_count / t;
     s = fill > kMaxSplits ? kMaxSplits : (fill < 2 ? 2 : (int)fill);

@@ -48,8 +48,8 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
   // a long K split it when the caller gave a workspace
   constexpr bool kCanSplit = !BKN && KIND != KIND_I4_E3M2 && KIND != KIND_I8_MOD;
   const int split_nks = (int)((row_bytes + 255) / 256);
-  if (kCanSplit && forced_config() < 0 && splitk_auto_splits(M, N, split_nks, dev.cu_count) > 1 &&
-      splitk_launch_splits(M, N, split_nks, dev.cu_count, ws, ws_bytes) > 1)
+  if (kCanSplit && forced_config() < 0 && splitk_auto_splits(M, N, split_nks, dev.cu_count, KIND) > 1 &&
+      splitk_launch_splits(M, N, split_nks, dev.cu_count, KIND, ws, ws_bytes) > 1)
     cfg = CFG_128_S2_R256_SPLITK;
   const int64_t stage_bytes = (KIND == KIND_I4 && expands_int4_in_lds(cfg)) ? K : row_bytes;
   const int rowb = stage_row_bytes(cfg);
@@ -182,7 +182,7 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         return launch_split<128, 128>(
             (const void*)&gemm_v3<KIND, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, kI4(1),
                                   false, true>,
-            args, 256, stream, splitk_launch_splits(M, N, args.k_stages, dev.cu_count, ws, ws_bytes), ws);
+            args, 256, stream, splitk_launch_splits(M, N, args.k_stages, dev.cu_count, KIND, ws, ws_bytes), ws);
       else
         return LPGEMM_ERROR_LAUNCH;
     case CFG_256_S4_R64:

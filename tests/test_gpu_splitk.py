@@ -53,11 +53,18 @@ def _split_shape(M, N):
     return M > 64 and _tiles(M, N) <= 64 and (M <= 128 or _tiles64(M, N) > 64)
 
 
-def _expected_splits(M, N, row_bytes):
-    # ... and at least 32 K-stages of 256 bytes: then 4 parts
+def _expected_splits(M, N, row_bytes, kind="i8"):
+    # ... and at least 32 K-stages of 256 bytes: then 4 parts, but below 64
+    # stages only while the unsplit choice's 128 x 64 tiles fill less than
+    # half the CUs (int4, which keeps 64 x 64 tiles, always)
     if not _split_shape(M, N):
         return 1
-    return 4 if (row_bytes + 255) // 256 >= 32 else 1
+    nks = (row_bytes + 255) // 256
+    if nks < 32:
+        return 1
+    if nks < 64 and kind != "i4" and 2 * (-(-M // 128)) * (-(-N // 64)) >= 256:
+        return 1
+    return 4
 
 
 def _counters_zero(ws, M=None, N=None):
@@ -81,7 +88,8 @@ def test_workspace_query_matches_rule():
     assert lp.splitk_workspace_bytes(128, 14336) == 0   # 112 tiles: no split
     assert lp.splitk_workspace_bytes(300, 520) == 0     # 45 tiles of 64 x 64: the unsplit kernel splits K itself
     assert [_expected_splits(M, N, K) for M, N, K in SHAPES] == [4, 4, 4]
-    assert [_expected_splits(M, N, K // 2) for M, N, K in SHAPES] == [1, 4, 1]
+    assert [_expected_splits(M, N, K // 2, "i4") for M, N, K in SHAPES] == [1, 4, 1]
+    assert _expected_splits(1000, 1000, 8208) == 1   # 128 band tiles at 33 stages: unsplit
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -107,7 +115,7 @@ def test_i8_splitk_exact(M, N, K):
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_i4_splitk_exact(M, N, K):
     K = (K + 31) // 32 * 32
-    _say("i4 split-K", M, N, K, "splits", _expected_splits(M, N, K // 2))
+    _say("i4 split-K", M, N, K, "splits", _expected_splits(M, N, K // 2, "i4"))
     q = inputs.int4_problem(M, N, K, seed=M + 2 * N + K)
     a, b = _dev(q.a_packed), _dev(q.b_packed)
     ws = lp.splitk_workspace(M, N)

@@ -289,7 +289,12 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int64_t K, int cu_count, in
   // 2.89 against 3.53 us, int4 2.87 against 3.79, fp16 3.43 against 4.70;
   // int8 512 x 512 x 16384 21.7 against 63.8 us; 768^3, with 144 tiles,
   // stays faster on 64 x 64: 4.23 against 5.26 us)
-  if ((int64_t)tiles(M, 64) * tiles(N, 64) <= cu_count / 2) return CFG_SKINNY_PIPE_W8R1;
+  // int4 from K = 4096 on too, whose band choice is this (graph-timed, one
+  // MI355X: int4 1024 x 1024 x 4096 720 against 600 TOP/s on 64 x 64 tiles,
+  // 768 x 768 x 8192 609 against 377, 1024 x 1024 x 16384 870 against 578;
+  // 1024^3 350 against 371 the other way)
+  if ((int64_t)tiles(M, 64) * tiles(N, 64) <= cu_count / 2 || (kind == KIND_I4 && K >= 4096))
+    return CFG_SKINNY_PIPE_W8R1;
   return CFG_V1_64x64;
 }
 

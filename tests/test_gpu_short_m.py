@@ -97,3 +97,16 @@ def test_band_tiles_small_grids(M, N, K2):
     got = out.cpu().numpy()
     ref = oracle.gemm_i8(q.a.astype(np.int8), q.b_t.astype(np.int8), rows=rows).astype(np.float32)
     np.testing.assert_array_equal(got if rows is None else got[rows], ref)
+
+
+# int4 small grids from K = 4096 on take 32 x 32 tiles whose eight waves
+# split K (768 x 768 x 8192; 1000 x 1000 x 4096, ragged), sampled rows
+@pytest.mark.parametrize("M,N,K2", [(768, 768, 8192), (1000, 1000, 4096)])
+def test_i4_small_grids_long_k(M, N, K2):
+    print("[case] int4 small grid, long K", M, N, K2, flush=True)
+    rows = sorted({0, 1, 31, 32, 500, M - 1} | set(range(5, M, 89)))
+    p = inputs.int4_problem(M, N, K2, seed=M + N + K2)
+    out = lp.gemm_i4(_dev(p.a_packed), _dev(p.b_packed), K2,
+                     out=torch.full((M, N), -7, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy()[rows], oracle.gemm_i4(p.a_packed, p.b_packed, K2, rows=rows))

@@ -202,8 +202,12 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int64_t K, int cu_count, in
   if (f == CFG_256_S2_R128_PIN_E3M2 || f == CFG_256_S2_R128_PIN_KXN) return CFG_256_S2_R128;
   if (f >= 0) return (KernelCfg)f;
   // few rows against many columns: stream B with split-K workgroups, each
-  // owning an equal share of the columns where that helps (skinny_columns)
-  if (M <= 32) return CFG_SKINNY_PIPE_W4R2;
+  // owning an equal share of the columns where that helps (skinny_columns);
+  // int4, whose expansion adds ALU work per byte, with eight waves of one
+  // K-block per round (graph-timed, one MI355X: int4 16 x 14336 x 4096 333
+  // against 301 TOP/s with four waves of two, 32 x 14336 x 4096 522 against
+  // 490, 16 x 4096 x 4096 141 against 127)
+  if (M <= 32) return kind == KIND_I4 ? CFG_SKINNY_PIPE_W8R1 : CFG_SKINNY_PIPE_W4R2;
   // 33-64 rows: the 128-row band kernel below once its 64-column tiles
   // number more than half the CUs, else the skinny kernel over two 32-row
   // bands; int4 always the skinny kernel (graph-timed at K = 4096, one

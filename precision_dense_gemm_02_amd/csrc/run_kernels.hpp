@@ -219,8 +219,11 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       const int w = skinny_columns(N, dev.cu_count, 2);
       return launch_skinny((const void*)&gemm_skinny_pipe<KIND, 4, 2, false, 2>, args, 256, stream, w > 0 ? w : 64);
     }
-    case CFG_SKINNY_PIPE_W8R1:
-      return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 8, 1>, args, 512, stream);
+    case CFG_SKINNY_PIPE_W8R1: {
+      // as configuration 14 (int4's choice at M <= 32)
+      const int w = forced_config() < 0 && M <= 32 ? skinny_columns(N, dev.cu_count, 1) : 0;
+      return launch_skinny((const void*)&gemm_skinny_pipe<KIND, 8, 1>, args, 512, stream, w > 0 ? w : 32);
+    }
     case CFG_SKINNY_PIPE_W4R3:
       return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND, 4, 3>, args, 256, stream);
     case CFG_SKINNY_PIPE_W8R2:

@@ -208,15 +208,18 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int64_t K, int cu_count, in
   // against 301 TOP/s with four waves of two, 32 x 14336 x 4096 522 against
   // 490, 16 x 4096 x 4096 141 against 127)
   if (M <= 32) return kind == KIND_I4 ? CFG_SKINNY_PIPE_W8R1 : CFG_SKINNY_PIPE_W4R2;
+  // int4 keeps that kernel up to three 32-row bands (graph-timed, one
+  // MI355X: M = 48, 64, 96 at N = 14336, K = 4096: 532, 625, 684 TOP/s
+  // against 485, 589, 636 with four waves and 325, 424, 604 for the band
+  // kernel below; M = 128 782 against 842 for the band kernel)
+  if (kind == KIND_I4 && M <= 96) return CFG_SKINNY_PIPE_W8R1;
   // 33-64 rows: the 128-row band kernel below once its 64-column tiles
   // number more than half the CUs, else the skinny kernel over two 32-row
-  // bands; int4 always the skinny kernel (graph-timed at K = 4096, one
+  // bands (graph-timed at K = 4096, one
   // MI355X: dequant M = 64, N = 14336 512 TOP/s against 317 skinny and 242
   // for the earlier choice, the split-K kernel of 64-row tiles; fp16 there
-  // 329 against 176 TFLOP/s; N = 8192 (128 tiles) 317 against 343 skinny;
-  // int4 N = 14336 595 skinny against 423)
-  if (M <= 64)
-    return kind != KIND_I4 && (int64_t)tiles(N, 64) > cu_count / 2 ? CFG_128x64_S3_R256 : CFG_SKINNY_PIPE_W4R2;
+  // 329 against 176 TFLOP/s; N = 8192 (128 tiles) 317 against 343 skinny)
+  if (M <= 64) return (int64_t)tiles(N, 64) > cu_count / 2 ? CFG_128x64_S3_R256 : CFG_SKINNY_PIPE_W4R2;
   // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128, and
   // B streams in 256-byte pieces per stage (graph-timed, one MI355X, against
   // six 128-byte stages: dequant M = 128, K = 4096, N = 14336 19.2 against

@@ -296,6 +296,17 @@ int lpgemm_version(void);
 int lpgemm_config_count(void);
 int lpgemm_force_config(int config);
 
+/* The configuration the automatic choice per shape takes (whatever
+ * lpgemm_force_config has pinned) for an M x N x K product on a device with
+ * `cu_count` compute units, through the entry points without a workspace:
+ * kind 0 lpgemm_i8, 1 lpgemm_i4, 2 lpgemm_f16, 3 lpgemm_i8_dequant.  Host
+ * arithmetic only; no device is needed.  Returns -1 for another kind,
+ * cu_count < 1, M or N <= 0 (nothing is launched), K < 0 or sizes above
+ * 2^31 - 1.  The rules behind the choice are measured ones (the
+ * PTX-vs-WMMA summary page's one-knob method, applied per shape), so the
+ * value can change between library versions. */
+int lpgemm_auto_config(int kind, int64_t M, int64_t N, int64_t K, int cu_count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -93,6 +93,8 @@ def load_library():
         lib.lpgemm_config_count.restype = ctypes.c_int
         lib.lpgemm_force_config.argtypes = [ctypes.c_int]
         lib.lpgemm_force_config.restype = ctypes.c_int
+        lib.lpgemm_auto_config.argtypes = [ctypes.c_int, _i64, _i64, _i64, ctypes.c_int]
+        lib.lpgemm_auto_config.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -124,6 +126,16 @@ def force_config(config: int) -> int:
     """Pin kernel configuration `config` for later GEMM calls in this process
     (-1: automatic choice per shape); returns the previous setting."""
     return int(load_library().lpgemm_force_config(int(config)))
+
+
+AUTO_KINDS = {"i8": 0, "i4": 1, "f16": 2, "dq": 3}
+
+
+def auto_config(kind: str, M: int, N: int, K: int, cu_count: int) -> int:
+    """The configuration the automatic choice takes for an M x N x K product
+    of `kind` ("i8", "i4", "f16" or "dq") on `cu_count` compute units (-1:
+    nothing is launched or the arguments are out of range)."""
+    return int(load_library().lpgemm_auto_config(AUTO_KINDS[kind], int(M), int(N), int(K), int(cu_count)))
 
 
 def _check(status: int, what: str) -> None:

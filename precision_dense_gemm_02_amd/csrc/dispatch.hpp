@@ -198,12 +198,9 @@ inline int skinny_columns(int64_t N, int cu_count, int nb) {
   return 0;
 }
 
-inline KernelCfg choose_config(int64_t M, int64_t N, int64_t K, int cu_count, int kind) {
-  const int f = forced_config();
-  // configurations 45 and 46 differ from 0 only for the E3M2 kind and for
-  // K x N B
-  if (f == CFG_256_S2_R128_PIN_E3M2 || f == CFG_256_S2_R128_PIN_KXN) return CFG_256_S2_R128;
-  if (f >= 0) return (KernelCfg)f;
+// The automatic choice for the i8, i4, f16 and dequant kinds (no forced
+// configuration, no split-K workspace).
+inline KernelCfg auto_config(int64_t M, int64_t N, int64_t K, int cu_count, int kind) {
   // few rows against many columns: stream B with split-K workgroups, each
   // owning an equal share of the columns where that helps (skinny_columns);
   // int4, whose expansion adds ALU work per byte, with eight waves of one
@@ -306,6 +303,15 @@ inline KernelCfg choose_config(int64_t M, int64_t N, int64_t K, int cu_count, in
   if ((int64_t)tiles(M, 64) * tiles(N, 64) <= cu_count / 2 || (kind == KIND_I4 && K >= 4096))
     return CFG_SKINNY_PIPE_W8R1;
   return CFG_V1_64x64;
+}
+
+inline KernelCfg choose_config(int64_t M, int64_t N, int64_t K, int cu_count, int kind) {
+  const int f = forced_config();
+  // configurations 45 and 46 differ from 0 only for the E3M2 kind and for
+  // K x N B
+  if (f == CFG_256_S2_R128_PIN_E3M2 || f == CFG_256_S2_R128_PIN_KXN) return CFG_256_S2_R128;
+  if (f >= 0) return (KernelCfg)f;
+  return auto_config(M, N, K, cu_count, kind);
 }
 
 // Split-K over 128 x 128 tiles (configuration 60) for products with few

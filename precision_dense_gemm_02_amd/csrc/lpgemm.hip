@@ -498,9 +498,15 @@ const char* lpgemm_status_string(lpgemm_status status) {
   return "unknown status";
 }
 
-int lpgemm_version(void) { return 300; }
+int lpgemm_version(void) { return 301; }
 
 int lpgemm_config_count(void) { return CFG_COUNT; }
+
+int lpgemm_auto_config(int kind, int64_t M, int64_t N, int64_t K, int cu_count) {
+  if (kind < KIND_I8 || kind > KIND_I8_DEQUANT || cu_count < 1) return -1;
+  if (M <= 0 || N <= 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return -1;
+  return (int)auto_config(M, N, K, cu_count, kind);
+}
 
 int lpgemm_force_config(int config) {
   const int v = (config >= 0 && config < CFG_COUNT) ? config : -1;

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(lib):
                           "lpgemm_f64_emu_moduli",
                           "lpgemm_f64_emu_workspace",
                           "lpgemm_status_string", "lpgemm_version", "lpgemm_config_count",
-                          "lpgemm_force_config", "lpgemm_splitk_workspace", "lpgemm_i8_splitk",
+                          "lpgemm_force_config", "lpgemm_auto_config", "lpgemm_splitk_workspace", "lpgemm_i8_splitk",
                           "lpgemm_i4_splitk", "lpgemm_f16_splitk", "lpgemm_i8_dequant_splitk"}
     for n in names:
         assert hasattr(lib, n), n
@@ -47,7 +47,7 @@ def test_config_count_and_force_hook(lib):
 
 
 def test_version_and_strings(lib):
-    assert b.version() == 300
+    assert b.version() == 301
     for code in range(6):
         assert b.status_string(code)
     assert b.status_string(99) == "unknown status"

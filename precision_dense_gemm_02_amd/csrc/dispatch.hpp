@@ -139,7 +139,9 @@ enum KernelCfg {
   CFG_256x224_S2_R128 = 61,      // configuration 0 with 256 x 224 tiles (four waves of 64 x 224)
   CFG_256x224_S2_R128_PERSIST = 62,  // configuration 61 as a persistent grid (int4: 61)
   CFG_SKINNY_PIPE_W4R2_N2 = 63,  // configuration 14 with two 32-row B blocks per workgroup (up to 64 columns)
-  CFG_COUNT = 64
+  CFG_256x128_S3_R128 = 64,      // 4 waves, 256 x 128, 3 stages of 128-byte rows
+  CFG_128x256_S3_R128 = 65,      // 4 waves, 128 x 256, 3 stages of 128-byte rows
+  CFG_COUNT = 66
 };
 
 // Row bytes of one LDS K-stage for a configuration (the register-staged
@@ -228,13 +230,13 @@ inline KernelCfg auto_config(int64_t M, int64_t N, int64_t K, int cu_count, int 
   if (M <= 128) return CFG_128x64_S3_R256;
   const int64_t big = (int64_t)tiles(M, 256) * tiles(N, 256);
   // N a multiple of 224 (the LLM projection's 14336 = 64 x 224): 256 x 224
-  // tiles once they fill at least half the CUs and their rounds of one tile
+  // tiles once they fill more than half the CUs and their rounds of one tile
   // per CU, each 7/8 of a 256 x 256 round's work, add up to less (M = 2048:
   // 512 tiles in two full rounds against 448 in 1.75), on the persistent
   // grid when they fill two or more whole rounds (int4: the plain grid).  Graph-timed,
   // K = 4096, one MI355X: dequant M = 1024 1959 TOP/s against 1950 with
   // 256 x 256 tiles and 1329 with 128 x 128; M = 768 1808 against 1752 and
-  // 1332; M = 512 (128 tiles) 1456 against 1404 for 128 x 128 tiles;
+  // 1332; M = 512 (128 tiles, half the CUs) takes the half-size tiles below;
   // M = 1536 (1.5 rounds) 1725 plain against 1568 persistent; int8
   // M = 4096 2156 against 2064 on the persistent 256 x 256 grid (3.5
   // rounds); the persistent 224 grid 2-3.5% ahead of the plain one at
@@ -244,7 +246,7 @@ inline KernelCfg auto_config(int64_t M, int64_t N, int64_t K, int cu_count, int 
     const int64_t t224 = (int64_t)tiles(M, 256) * (N / 224);
     const int64_t r256 = (big + cu_count - 1) / cu_count;
     const int64_t r224 = (t224 + cu_count - 1) / cu_count;
-    if (2 * t224 >= cu_count && 7 * r224 < 8 * r256)
+    if (2 * t224 > cu_count && 7 * r224 < 8 * r256)
       return t224 >= 2 * (int64_t)cu_count && t224 % cu_count == 0 ? CFG_256x224_S2_R128_PERSIST
                                                                     : CFG_256x224_S2_R128;
   }
@@ -264,6 +266,22 @@ inline KernelCfg auto_config(int64_t M, int64_t N, int64_t K, int cu_count, int 
   if (2 * big > cu_count) {
     if (big >= 2 * (int64_t)cu_count && big % cu_count == 0 && kind != KIND_I4) return CFG_256_S2_R128_PERSIST;
     return CFG_256_S2_R128;
+  }
+  // half-size large tiles, 128 x 256 (int4: 256 x 128) with three 128-byte
+  // stages, when they make more than half a round and at most one, at
+  // K >= 2048 (graph-timed, one MI355X, against the earlier choice: int8 2048 x 4096
+  // x 4096 1716 against 1480 TOP/s, 1536 x 4096 x 4096 1517 against 1319,
+  // 1280 x 4096 x 4096 1442 against 1211, 2048 x 4096 x 2048 1487 against
+  // 1200; dequant 512 x 14336 x 4096 1626 against 1458 on 256 x 224 tiles
+  // (128 of them), 768 x 8192 x 4096 1570 against 1352; fp16 1536 x 4096 x
+  // 4096 887 against 786 TFLOP/s; int4 2048 x 4096 x 4096 2037 against
+  // 1739; a full round and more lost: int8 1536 x 6144 x 2048, 288 tiles,
+  // 1026 against 1383 for 256 x 256 tiles, and half a round: 2048^3 1000
+  // against 1086)
+  {
+    const bool i4 = kind == KIND_I4;
+    const int64_t t_half = i4 ? (int64_t)tiles(M, 256) * tiles(N, 128) : (int64_t)tiles(M, 128) * tiles(N, 256);
+    if (K >= 2048 && 2 * t_half > cu_count && t_half <= cu_count) return i4 ? CFG_256x128_S3_R128 : CFG_128x256_S3_R128;
   }
   // 128 x 64 tiles with three 256-byte stages (the 128-row band kernel)
   // when they make between a quarter of a round and one round, at K >=

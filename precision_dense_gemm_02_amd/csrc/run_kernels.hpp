@@ -106,6 +106,10 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
           stream);
     case CFG_128_S4_R128:
       return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 4, 128>, args, 256, stream);
+    case CFG_256x128_S3_R128:
+      return launch<256, 128>((const void*)&gemm_v3<KIND, 256, 128, 3, 128, 0, false, false, 0, kNtC>, args, 256, stream);
+    case CFG_128x256_S3_R128:
+      return launch<128, 256>((const void*)&gemm_v3<KIND, 128, 256, 3, 128, 0, false, false, 0, kNtC>, args, 256, stream);
     case CFG_256x224_S2_R128:
       return launch<256, 224>(
           (const void*)&gemm_v3<KIND, 256, 224, 2, 128, 0, false, false, 2, kNtC, 0, false, kPinLoads>, args, 256,

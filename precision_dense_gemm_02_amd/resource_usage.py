@@ -31,6 +31,10 @@ DEFAULT_KERNELS = {
     "lpgemm::gemm_v3<2, 256, 224, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false, false>": "fp16, N a multiple of 224, persistent",
     "lpgemm::gemm_v3<3, 256, 224, 2, 128, 0, false, false, 2, true, 0, false, true, true, 0, false, false>": "dequant int8, N a multiple of 224 (LLM M = 2048), persistent",
     "lpgemm::gemm_v3<1, 256, 224, 2, 128, 0, false, false, 2, false, 0, false, false, false, 0, false, false>": "int4, N a multiple of 224",
+    "lpgemm::gemm_v3<0, 128, 256, 3, 128, 0, false, false, 0, true, 0, false, false, false, 0, false, false>": "int8, half a round to one round of 128x256 tiles",
+    "lpgemm::gemm_v3<1, 256, 128, 3, 128, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "int4, half a round to one round of 256x128 tiles",
+    "lpgemm::gemm_v3<2, 128, 256, 3, 128, 0, false, false, 0, true, 0, false, false, false, 0, false, false>": "fp16, half a round to one round of 128x256 tiles",
+    "lpgemm::gemm_v3<3, 128, 256, 3, 128, 0, false, false, 0, true, 0, false, false, false, 0, false, false>": "dequant int8, half a round to one round of 128x256 tiles",
     "lpgemm::gemm_v3<0, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "int8, 128x128 tiles (2048^3)",
     "lpgemm::gemm_v3<2, 128, 128, 4, 128, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "fp16, 128x128 tiles (2048^3)",
     "lpgemm::gemm_v3<1, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 1, false, false>": "int4, 128x128 tiles (2048^3), 32-byte fragment reads",

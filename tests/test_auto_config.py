@@ -20,7 +20,12 @@ TABLE = [
     ("dq", 2048, 14336, 4096, 62, "N = 64 x 224: two whole rounds of 256 x 224 tiles"),
     ("dq", 1536, 14336, 4096, 61, "1.5 rounds of 256 x 224 tiles: plain"),
     ("dq", 1024, 14336, 4096, 61, "one round of 256 x 224 tiles"),
-    ("dq", 512, 14336, 4096, 61, "128 tiles of 256 x 224, half the CUs"),
+    ("dq", 512, 14336, 4096, 65, "128 tiles of 256 x 224, only half the CUs: 224 of 128 x 256"),
+    ("i8", 2048, 4096, 4096, 65, "256 tiles of 128 x 256: one round of half-size large tiles"),
+    ("i8", 1536, 4096, 4096, 65, "192 of them, three quarters of a round"),
+    ("i4", 2048, 4096, 4096, 64, "int4: 256 x 128"),
+    ("i8", 1024, 4096, 4096, 22, "128 half-size tiles, half the CUs: 128 x 128"),
+    ("i8", 1536, 6144, 2048, 0, "144 large tiles: 256 x 256"),
     ("dq", 8192, 14336, 4096, 47, "seven whole rounds of 256 x 256 beat eight of 224"),
     ("i4", 2048, 14336, 4096, 62, "int4 too (configuration 62 runs 61's plain grid for int4)"),
     ("dq", 256, 14336, 4096, 22, "64 tiles of 224: 128 x 128 tiles, four 128-byte stages"),

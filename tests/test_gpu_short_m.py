@@ -2,8 +2,8 @@
 33-64 rows take the 128-row band kernel (128 x 64 tiles, three 256-byte
 stages) once its tiles number more than half the CUs and the skinny kernel
 over two 32-row bands otherwise (int4: always the skinny kernel); 65-128
-rows the band kernel for every kind, and so do small grids above 128 rows
-(below).  Integer kinds bit for bit, fp16 on
+rows the band kernel for every kind, and so do small grids above 128 rows;
+half-size large tiles between half a round and one (below).  Integer kinds bit for bit, fp16 on
 integer-valued operands (exact in fp32) and on random ones within the
 bound; C is filled beforehand so that an unwritten element shows."""
 import numpy as np
@@ -110,3 +110,32 @@ def test_i4_small_grids_long_k(M, N, K2):
                      out=torch.full((M, N), -7, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy()[rows], oracle.gemm_i4(p.a_packed, p.b_packed, K2, rows=rows))
+
+
+# Between half a round and one round of 128 x 256 tiles (int4: 256 x 128)
+# at K >= 2048: the half-size large tiles (on 256 CUs: 2048 x 4096, 256
+# tiles; 1500 x 4100, 192, ragged on both sides), sampled rows
+@pytest.mark.parametrize("M,N,K2", [(2048, 4096, 4096), (1500, 4100, 2064)])
+def test_half_size_large_tiles(M, N, K2):
+    print("[case] half-size large tiles", M, N, K2, flush=True)
+    rows = sorted({0, 1, 127, 128, 255, 256, M - 1} | set(range(7, M, 113)))
+    p = inputs.int8_problem(M, N, K2, seed=M + N + K2, scales=True)
+    out = lp.gemm_i8(_dev(p.a), _dev(p.b_t), out=torch.full((M, N), -7, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy()[rows], oracle.gemm_i8(p.a, p.b_t, rows=rows))
+    out = lp.gemm_i8_dequant(_dev(p.a), _dev(p.b_t), _dev(p.row_scale), _dev(p.col_scale),
+                             out=torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    ref = oracle.gemm_i8_dequant(p.a, p.b_t, p.row_scale, p.col_scale, rows=rows)
+    np.testing.assert_array_equal(out.cpu().numpy()[rows].view(np.uint32), ref.view(np.uint32))
+    q = inputs.f16_integer_problem(M, N, K2, seed=M + N + K2 + 1)
+    out = lp.gemm_f16(_dev(q.a), _dev(q.b_t), out=torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    ref = oracle.gemm_i8(q.a.astype(np.int8), q.b_t.astype(np.int8), rows=rows).astype(np.float32)
+    np.testing.assert_array_equal(out.cpu().numpy()[rows], ref)
+    K4 = (K2 + 31) // 32 * 32
+    r = inputs.int4_problem(M, N, K4, seed=M + N + K4 + 2)
+    out = lp.gemm_i4(_dev(r.a_packed), _dev(r.b_packed), K4,
+                     out=torch.full((M, N), -7, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy()[rows], oracle.gemm_i4(r.a_packed, r.b_packed, K4, rows=rows))

@@ -2192,27 +2192,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_lds(GemmArgs p) {
   skinny_reduce_store_strided<KIND, MT, NT, WAVES, kPitch, kWaveLds / 4>(p, red, m0, n0);
 }
 
-// A 16-byte buffer load into registers issued as inline asm, so that the
-// compiler neither counts it nor places waits for it: the caller waits with
-// wait_vmcnt and then pins the destination with pin_after_wait before any
-// use (the data lands some time after the instruction issues).
-//
-// The invariant this relies on: between the load and its pin, the compiler
-// must not copy, spill or move `dst` (it believes the value is already
-// there, so a copy made before the data lands would read stale bits).  The
-// skinny kernels keep their in-flight fragments in fixed, unrolled slots
-// (no dynamic indexing), hold few registers (no pressure to split live
-// ranges), and the bit-exact GPU tests of the M <= 32 path and of the fused
-// W8A8 kernel fail if a toolchain ever breaks it.  The compiler-tracked load
-// builtin would be safe by construction, but the compiler does not count
-// the direct-to-LDS copies in between, so the wait it places before a
-// fragment's first use would also wait for the next round's loads.
-__device__ __forceinline__ void load_16_async(i32x4& dst, const i32x4& rsrc, uint32_t voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(voff), "s"(rsrc) : "memory");
-}
-// Tells the compiler that `x` changes here, so no use of it (or copy of it)
-// is scheduled before the preceding wait.
-__device__ __forceinline__ void pin_after_wait(i32x4& x) { asm volatile("" : "+v"(x)); }
 
 // ---------------------------------------------------------------------------
 // Per-row int8 quantisation of fp16 activations (the step in front of a W8A8
@@ -2259,10 +2238,12 @@ __device__ __forceinline__ float wave_max(float v) {
 // Skinny-M kernel, B through LDS as in gemm_skinny_lds, with the rounds of
 // each wave double-buffered: the copies and A loads of round i+1 are in
 // flight while round i is read back and contracted, so the weight stream
-// does not stop at every round.  Two LDS regions of R K-blocks per wave; all
-// loads of the loop are inline asm (counted only by the explicit waits):
-// after issuing round i+1, vmcnt(8R) leaves exactly round i+1's 8R loads
-// outstanding, so round i has landed.
+// does not stop at every round.  Two LDS regions of R K-blocks per wave for
+// B (direct-to-LDS copies, counted only by the explicit waits); A's
+// fragments come through the compiler-tracked register load, two rounds
+// ahead in three register sets (one round ahead in two for the eight-wave
+// int4 kernel and three-block rounds), in an issue order under which the
+// compiler's own waits for them never hold back the next round's copies.
 //
 // QA: A holds fp16 activations (M x K binary16) that the kernel quantises
 // per row itself, the W8A8 step in one launch (KIND_I8_DEQUANT only).  Each
@@ -2294,11 +2275,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   constexpr int kRoundLds = R * kBlockLds;
   constexpr int kWaveLds = 2 * kRoundLds;
   constexpr int kAParts = QA ? 2 : 1;         // 16-byte loads per A fragment
-  constexpr int kLoadsPerRound = (4 * NB + 4 * kAParts) * R;   // 4 NB copies + the A fragments per block
+  constexpr int kLoadsB = 4 * NB * R;          // B copies per round (4 per 32 rows and block)
+  constexpr int kLoadsA = 4 * kAParts * R;     // A fragment loads per round
   static_assert(kWaveLds >= MT * kPitch * 4, "the partial sums reuse the wave's region");
-  // two rounds can be outstanding at once; the vector-memory counter holds
-  // at most 63, and a wait on a counter that has overflowed passes too early
-  static_assert(2 * kLoadsPerRound <= 63, "two rounds of loads must fit the vmcnt counter");
+  // at most three rounds of A and two of B are outstanding at once; the
+  // vector-memory counter holds at most 63, and a wait on a counter that
+  // has overflowed passes too early
+  static_assert(3 * kLoadsA + 2 * kLoadsB <= 63, "the loads in flight must fit the vmcnt counter");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[WAVES * kWaveLds];
 
@@ -2312,7 +2295,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   const int rows_b = min(tile_w, p.N - n0);
   // bytes per row of A: K (int8) or 2K (binary16)
   const uint32_t a_stride = (uint32_t)p.row_bytes * kAParts;
-  const i32x4 rsrc_a = make_rsrc(p.A + (size_t)m0 * a_stride, rows_a * a_stride);
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.A + (size_t)m0 * a_stride), 0, rows_a * a_stride, kBufferWord3);
   const i32x4 rsrc_b = make_rsrc(p.B + (size_t)n0 * p.row_bytes, rows_b * p.row_bytes);
   uint8_t* const my_smem = smem + wave * kWaveLds;
   const uint32_t my_lds = lds_address(my_smem);
@@ -2366,10 +2350,39 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][nb][0][e] = 0;
 
-  i32x4 fa[2][R][1][4 * kAParts];
+  // A's fragments go straight into registers through the compiler-tracked
+  // load; B's blocks go into LDS through direct copies, one round ahead, in
+  // two regions (round x in region x % 2).  The compiler does not count the
+  // copies, so before A(i)'s first use it waits until no more A loads are
+  // outstanding than it issued after A(i); the issue order below makes that
+  // wait no stricter than the explicit one for B(i) (with no more B copies
+  // than A loads per round, one B block), so the next copies stay in flight.
+  //
+  // kAhead = 2 (three A register sets, round x in set x % 3): the step for
+  // round i issues B(i + 1), then A(i + 2), waits until only A(i + 1),
+  // B(i + 1) and A(i + 2) may be outstanding (B(i) has landed; the compiler
+  // adds A(i + 1), issued right after B(i)), and contracts round i.  No load
+  // is issued past the last round, as such a load moves no data but costs
+  // the CU's load path as much as one that does: the last rounds are
+  // straight-line code with the issue pattern fixed at compile time (a
+  // branch around an A load would leave the compiler unsure whether it is
+  // in flight, and it would then wait for everything before the next use).
+  //
+  // kAhead = 1 (two sets: for the eight-wave int4 kernel, whose registers
+  // must stay within 128 for two workgroups per CU, and for three blocks
+  // per round, where three sets would spill): the step issues
+  // A(i + 1), then B(i + 1) while rounds remain (the compiler does not
+  // track the copies, so their branch costs nothing), waits for B(i), and
+  // contracts round i; the compiler adds A(i + 1).  Its A loads run one
+  // round past the end (outside A, no data moves) and are consumed at the
+  // end.
+  //
+  // Either way every A load issued is used later, so the compiler drops
+  // none and the explicit counts hold.
+  constexpr int kAhead = ((KIND == KIND_I4 && WAVES == 8) || R >= 3) ? 1 : 2;
+  i32x4 fa[kAhead + 1][R][1][4 * kAParts];
 
-  // round i: K-blocks b0 + R i .. + R - 1 into region `buf`
-  auto issue = [&](int i, auto buf_c) {
+  auto issue_a = [&](int i, auto buf_c) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -2382,40 +2395,38 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
         const bool ok = in_range && col < row_bytes;
 #pragma unroll
         for (int part = 0; part < kAParts; ++part)
-          load_16_async(fa[buf][j][0][kAParts * q + part], rsrc_a,
-                        ok ? a_row + kAParts * col + 16 * part : kOutOfRange);
-      }
-#pragma unroll
-      for (int t = 0; t < 4 * NB; ++t) {
-        const bool ok = in_range && kbyte + dma_col[t] < row_bytes;
-        lds_dma_16(rsrc_b, my_lds + buf * kRoundLds + j * kBlockLds + t * 1024,
-                   ok ? dma_off[t] + kbyte : kOutOfRange);
+          fa[buf][j][0][kAParts * q + part] = __builtin_amdgcn_raw_buffer_load_b128(
+              rsrc_a, ok ? a_row + kAParts * col + 16 * part : kOutOfRange, 0, 0);
       }
     }
   };
-  // contract round i from region `buf`, first starting round i + 1 (if any)
-  // in the other region
-  auto step = [&](int i, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    if (i + 1 < rounds) {
-      wait_lgkmcnt0();   // the other region's fragment reads (round i - 1) are complete
-      issue(i + 1, std::integral_constant<int, 1 - buf>());
-      wait_vmcnt<kLoadsPerRound>();
-    } else {
-      wait_vmcnt<0>();
+  auto issue_b = [&](int i) __attribute__((always_inline)) {
+    const uint32_t region = my_lds + (uint32_t)(i & 1) * kRoundLds;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int blk = b0 + R * i + j;
+      const uint32_t kbyte = (uint32_t)blk * kBlock;
+      const bool in_range = blk < b1;
+#pragma unroll
+      for (int t = 0; t < 4 * NB; ++t) {
+        const bool ok = in_range && kbyte + dma_col[t] < row_bytes;
+        lds_dma_16(rsrc_b, region + j * kBlockLds + t * 1024, ok ? dma_off[t] + kbyte : kOutOfRange);
+      }
     }
+  };
+  // contract round i from A set `set` and B region i % 2
+  auto contract = [&](int i, auto set_c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
+    const uint8_t* const region = my_smem + (i & 1) * kRoundLds;
     i32x4 fb[R][NB][4];
 #pragma unroll
     for (int j = 0; j < R; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int part = 0; part < kAParts; ++part) pin_after_wait(fa[buf][j][0][kAParts * q + part]);
+      for (int q = 0; q < 4; ++q)
         // block nb's rows start 32 rows on, which leaves the swizzle unchanged
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          fb[j][nb][q] = *(const i32x4*)(my_smem + buf * kRoundLds + j * kBlockLds + nb * 32 * kBlock + frag_off[q]);
-      }
+          fb[j][nb][q] = *(const i32x4*)(region + j * kBlockLds + nb * 32 * kBlock + frag_off[q]);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       if constexpr (QA) {
@@ -2423,23 +2434,115 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
         i32x4 qa[1][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint64_t lo = qs != 0.f ? quantize8(__builtin_bit_cast(f16x8, fa[buf][j][0][2 * q]), qs, qr) : 0;
-          const uint64_t hi = qs != 0.f ? quantize8(__builtin_bit_cast(f16x8, fa[buf][j][0][2 * q + 1]), qs, qr) : 0;
+          const uint64_t lo = qs != 0.f ? quantize8(__builtin_bit_cast(f16x8, fa[set][j][0][2 * q]), qs, qr) : 0;
+          const uint64_t hi = qs != 0.f ? quantize8(__builtin_bit_cast(f16x8, fa[set][j][0][2 * q + 1]), qs, qr) : 0;
           qa[0][q] = i32x4{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) skinny_block<KIND, 1>(acc[j][nb], qa, fb[j][nb]);
       } else {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) skinny_block<KIND, 1>(acc[j][nb], fa[buf][j], fb[j][nb]);
+        for (int nb = 0; nb < NB; ++nb) skinny_block<KIND, 1>(acc[j][nb], fa[set][j], fb[j][nb]);
       }
     }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
 
-  if (rounds > 0) issue(0, std::integral_constant<int, 0>());
-  for (int i = 0; i < rounds; i += 2) {
-    step(i, std::integral_constant<int, 0>());
-    if (i + 1 < rounds) step(i + 1, std::integral_constant<int, 1>());
+  if constexpr (kAhead == 2) {
+    // kFull: issue B(i + 1) and A(i + 2); kSecondLast: only B(i + 1);
+    // kLast: nothing
+    constexpr int kFull = 0, kSecondLast = 1, kLast = 2;
+    auto step = [&](int i, auto set_c, auto mode_c) __attribute__((always_inline)) {
+      constexpr int set = decltype(set_c)::value;
+      constexpr int mode = decltype(mode_c)::value;
+      __builtin_amdgcn_sched_barrier(0);   // steps do not interleave (fewer live registers)
+      if constexpr (mode == kFull) {
+        wait_lgkmcnt0();   // the other region's fragment reads (round i - 1) are complete
+        issue_b(i + 1);
+        issue_a(i + 2, std::integral_constant<int, (set + 2) % 3>());
+        wait_vmcnt<2 * kLoadsA + kLoadsB>();   // all but A(i + 1), B(i + 1), A(i + 2)
+      } else if constexpr (mode == kSecondLast) {
+        wait_lgkmcnt0();
+        issue_b(i + 1);
+        wait_vmcnt<kLoadsA + kLoadsB>();       // all but A(i + 1), B(i + 1)
+      } else {
+        wait_vmcnt<0>();
+      }
+      contract(i, set_c);
+    };
+    using Full = std::integral_constant<int, kFull>;
+    using SecondLast = std::integral_constant<int, kSecondLast>;
+    using Last = std::integral_constant<int, kLast>;
+    if (rounds > 0) {
+      issue_a(0, I0());
+      issue_b(0);
+      issue_a(1, I1());   // (a single round: outside A, no data moves)
+      // whole groups of three full steps while two more rounds follow them;
+      // the loop's back edge comes only from a whole group, so the
+      // compiler's view of the loads in flight is the same at every loop head
+      int i = 0;
+      for (; i + 5 <= rounds; i += 3) {
+        step(i, I0(), Full());
+        step(i + 1, I1(), Full());
+        step(i + 2, I2(), Full());
+      }
+      // the last one to four rounds, each case straight-line
+      switch (rounds - i) {
+        case 4:
+          step(i, I0(), Full());
+          step(i + 1, I1(), Full());
+          step(i + 2, I2(), SecondLast());
+          step(i + 3, I0(), Last());
+          break;
+        case 3:
+          step(i, I0(), Full());
+          step(i + 1, I1(), SecondLast());
+          step(i + 2, I2(), Last());
+          break;
+        case 2:
+          step(i, I0(), SecondLast());
+          step(i + 1, I1(), Last());
+          break;
+        default:
+          step(i, I0(), Last());
+          break;
+      }
+    }
+  } else {
+    auto step = [&](int i, auto set_c) __attribute__((always_inline)) {
+      constexpr int set = decltype(set_c)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkmcnt0();   // the other region's fragment reads (round i - 1) are complete
+      issue_a(i + 1, std::integral_constant<int, 1 - set>());
+      if (i + 1 < rounds) {
+        issue_b(i + 1);
+        wait_vmcnt<kLoadsA + kLoadsB>();   // all but A(i + 1), B(i + 1)
+      } else {
+        wait_vmcnt<kLoadsA>();
+      }
+      contract(i, set_c);
+    };
+    if (rounds > 0) {
+      issue_a(0, I0());
+      issue_b(0);
+      // whole pairs, then the rest; the loop's back edge comes only from a
+      // whole pair
+      int i = 0;
+      for (; i + 2 <= rounds; i += 2) {
+        step(i, I0());
+        step(i + 1, I1());
+      }
+      if (i < rounds) step(i, I0());
+      wait_vmcnt<0>();
+#pragma unroll
+      for (int set = 0; set < 2; ++set)
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+          for (int q = 0; q < 4 * kAParts; ++q) asm volatile("" ::"v"(fa[set][j][0][q]));
+    }
   }
 #pragma unroll
   for (int j = 1; j < R; ++j)

@@ -209,7 +209,15 @@ inline KernelCfg auto_config(int64_t M, int64_t N, int64_t K, int cu_count, int 
   // K-block per round (graph-timed, one MI355X: int4 16 x 14336 x 4096 333
   // against 301 TOP/s with four waves of two, 32 x 14336 x 4096 522 against
   // 490, 16 x 4096 x 4096 141 against 127)
-  if (M <= 32) return kind == KIND_I4 ? CFG_SKINNY_PIPE_W8R1 : CFG_SKINNY_PIPE_W4R2;
+  // The other kinds take eight waves too when the 32-column tiles number at
+  // most half the CUs: more waves per CU then stream B (graph-timed, one
+  // MI355X: int8 32 x 4096 x 4096 6.98 against 7.59 us, dequant
+  // 16 x 4096 x 14336 13.77 against 14.45, fp16 16 x 4096 x 4096 8.72
+  // against 8.89, dequant 32 x 2048 x 8192 10.92 against 11.19; at N = 8192
+  // four waves stay ahead, int8 32 x 8192 x 8192 14.04 against 15.41).
+  const bool few_columns = (int64_t)tiles(N, 32) <= cu_count / 2;
+  if (M <= 32)
+    return kind == KIND_I4 || few_columns ? CFG_SKINNY_PIPE_W8R1 : CFG_SKINNY_PIPE_W4R2;
   // int4 keeps that kernel up to three 32-row bands (graph-timed, one
   // MI355X: M = 48, 64, 96 at N = 14336, K = 4096: 532, 625, 684 TOP/s
   // against 485, 589, 636 with four waves and 325, 424, 604 for the band
@@ -221,7 +229,12 @@ inline KernelCfg auto_config(int64_t M, int64_t N, int64_t K, int cu_count, int 
   // MI355X: dequant M = 64, N = 14336 512 TOP/s against 317 skinny and 242
   // for the earlier choice, the split-K kernel of 64-row tiles; fp16 there
   // 329 against 176 TFLOP/s; N = 8192 (128 tiles) 317 against 343 skinny)
-  if (M <= 64) return (int64_t)tiles(N, 64) > cu_count / 2 ? CFG_128x64_S3_R256 : CFG_SKINNY_PIPE_W4R2;
+  // (and there, as above, eight waves at few columns: int8 64 x 4096 x 4096
+  // 7.05 against 7.47 us, dequant 64 x 4096 x 14336 18.67 against 19.02)
+  if (M <= 64)
+    return (int64_t)tiles(N, 64) > cu_count / 2 ? CFG_128x64_S3_R256
+           : few_columns                         ? CFG_SKINNY_PIPE_W8R1
+                                                 : CFG_SKINNY_PIPE_W4R2;
   // a 128-row band: 128 x 64 tiles double the workgroups of 128 x 128, and
   // B streams in 256-byte pieces per stage (graph-timed, one MI355X, against
   // six 128-byte stages: dequant M = 128, K = 4096, N = 14336 19.2 against

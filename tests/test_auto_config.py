@@ -45,6 +45,10 @@ TABLE = [
     ("dq", 64, 14336, 4096, 34, "33-64 rows, 224 band tiles: the band kernel"),
     ("dq", 64, 8192, 4096, 14, "33-64 rows, 128 band tiles: the skinny kernel"),
     ("dq", 16, 14336, 4096, 14, "M <= 32: the skinny kernel"),
+    ("i8", 32, 8192, 8192, 14, "256 column tiles of 32: four waves"),
+    ("i8", 32, 4096, 4096, 15, "128 column tiles, half the CUs: eight waves"),
+    ("dq", 16, 4096, 14336, 15, "the same at K = 14336"),
+    ("i8", 64, 4096, 4096, 15, "33-64 rows at few columns: eight waves"),
     ("i4", 16, 14336, 4096, 15, "int4 at M <= 32: eight waves"),
 ]
 

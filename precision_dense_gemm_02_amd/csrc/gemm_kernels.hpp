@@ -2256,6 +2256,15 @@ __device__ __forceinline__ float wave_max(float v) {
 // bit.  The scan is repeated by every workgroup of a row band (the cost the
 // Day-12 page ascribes to a quantisation prologue inside the GEMM).
 //
+// BCPOL: cache policy of the B copies (see lds_dma_16).  The four-wave
+// kernel the automatic choice takes at many columns streams B
+// non-temporally: the weights of a skinny product are read once per call,
+// and from HBM (graph-timed, one MI355X, weights cold: LLM M = 16 12.88
+// against 14.03 us, fp16 16 x 14336 x 4096 21.75 against 23.93, int8
+// 32 x 8192 x 8192 16.31 against 17.35); re-read from the Infinity Cache
+// call after call they gain or lose a few percent (-9% to +6%).  The
+// eight-wave kernel keeps the default: warm, it lost 11-25% with them.
+//
 // NB, p.tile_w: a workgroup holds NB 32-row blocks of B and owns p.tile_w
 // (at most 32 NB) columns of C from column p.tile_w * (its tile column) on;
 // B rows past its columns read as zero without touching memory and their
@@ -2263,7 +2272,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // B rows, so a column width that divides N into as many workgroups as
 // there are CUs (N = 14336 on 256 CUs: 56 columns, NB = 2) loads every CU
 // equally, where 32-column tiles (448) give some CUs two and others one.
-template <int KIND, int WAVES, int R, bool QA = false, int NB = 1>
+template <int KIND, int WAVES, int R, bool QA = false, int NB = 1, int BCPOL = 0>
 __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
   using Acc = typename KindTraits<KIND>::Acc;
   static_assert(!QA || KIND == KIND_I8_DEQUANT, "on-the-fly quantisation feeds the dequantising product");
@@ -2410,7 +2419,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_pipe(GemmArgs p) {
 #pragma unroll
       for (int t = 0; t < 4 * NB; ++t) {
         const bool ok = in_range && kbyte + dma_col[t] < row_bytes;
-        lds_dma_16(rsrc_b, region + j * kBlockLds + t * 1024, ok ? dma_off[t] + kbyte : kOutOfRange);
+        lds_dma_16<BCPOL>(rsrc_b, region + j * kBlockLds + t * 1024, ok ? dma_off[t] + kbyte : kOutOfRange);
       }
     }
   };

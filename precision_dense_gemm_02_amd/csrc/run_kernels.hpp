@@ -217,7 +217,7 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
       // the automatic choice's even column share for a single 32-row band
       // (forced, or more rows: 32 columns)
       const int w = forced_config() < 0 && M <= 32 ? skinny_columns(N, dev.cu_count, 1) : 0;
-      return launch_skinny((const void*)&gemm_skinny_pipe<KIND, 4, 2>, args, 256, stream, w > 0 ? w : 32);
+      return launch_skinny((const void*)&gemm_skinny_pipe<KIND, 4, 2, false, 1, 1>, args, 256, stream, w > 0 ? w : 32);
     }
     case CFG_SKINNY_PIPE_W4R2_N2: {
       const int w = skinny_columns(N, dev.cu_count, 2);

@@ -43,7 +43,7 @@ DEFAULT_KERNELS = {
     "lpgemm::gemm_v3<1, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 1, false, true>": "int4 split-K",
     "lpgemm::gemm_v3<2, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, true>": "fp16 split-K",
     "lpgemm::gemm_v3<3, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, true>": "dequant int8 split-K",
-    "lpgemm::gemm_skinny_pipe<3, 4, 2, false, 1>": "dequant int8, M <= 32 (LLM M = 16: 28 columns per workgroup)",
+    "lpgemm::gemm_skinny_pipe<3, 4, 2, false, 1, 1>": "dequant int8, M <= 32 (LLM M = 16: 28 columns per workgroup)",
     "lpgemm::gemm_tiled<0, 64, 64, 2, 2>": "int8, small grids (1024^3, 512^3)",
     "lpgemm::quantize_rows_f16_regs<4, 2>": "W8A8 row quantiser, short M",
     "lpgemm::quantize_rows_f16_regs<1, 8>": "W8A8 row quantiser, M = 2048",

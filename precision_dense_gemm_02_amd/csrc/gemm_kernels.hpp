@@ -579,9 +579,10 @@ struct RowLayout<64> {
   __device__ static int pos(int r, int c) { return c ^ f(r); }
 };
 
-// CPOL: cache policy of the operand loads (see lds_dma_16).  SPLIT: waves 0
-// and 1 load only A, waves 2 and 3 only B (needs BM == BN); by default every
-// wave loads its share of both.  These two are ablation knobs.
+// CPOL: cache policy of the operand loads (see lds_dma_16; 5: A default, B
+// non-temporal).  SPLIT: waves 0 and 1 load only A, waves 2 and 3 only B
+// (needs BM == BN); by default every wave loads its share of both.  These
+// two are ablation knobs.
 //
 // BKN: B is stored K x N row-major (N contiguous, int8) instead of
 // K-contiguous.  A stage then holds ROWB k-rows of the tile's BN columns of
@@ -826,7 +827,10 @@ __global__ __launch_bounds__(256) void gemm_v3(GemmArgs p) {
     }
     const i32x4 ra = next ? rsrc_a_next : rsrc_a;
     const i32x4 rb = next ? rsrc_b_next : rsrc_b;
-    lds_dma_16<CPOL>(is_a(t) ? ra : rb, smem_lds + ((gbase + s) % STAGES) * kStage + g * 1024, off);
+    // CPOL 5: A with the default policy, B non-temporal
+    constexpr int kCpolA = CPOL == 5 ? 0 : CPOL, kCpolB = CPOL == 5 ? 1 : CPOL;
+    if (is_a(t)) lds_dma_16<kCpolA>(ra, smem_lds + ((gbase + s) % STAGES) * kStage + g * 1024, off);
+    else lds_dma_16<kCpolB>(rb, smem_lds + ((gbase + s) % STAGES) * kStage + g * 1024, off);
   };
 
   // prefetch touch t of this wave covers operand rows 64 (kPf wave + t) ..

@@ -241,6 +241,14 @@ lpgemm_status run(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     case CFG_128x64_S8_R64:
       return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 8, 64>, args, 256, stream);
     case CFG_128x64_S3_R256:
+      // one row band (M <= 128): every B element is read by one workgroup,
+      // so B streams non-temporally (graph-timed, one MI355X, weights from
+      // HBM: LLM M = 128 17.83 against 18.55 us, fp16 128 x 14336 x 4096
+      // 30.0 against 31.2, int8 128 x 8192 x 8192 26.6 against 29.6; with
+      // the weights in the Infinity Cache 3-16% slower; above 128 rows B is
+      // re-read by every row band and keeps the default policy)
+      if (M <= 128)
+        return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 3, 256, 5>, args, 256, stream);
       return launch<128, 64>((const void*)&gemm_v3<KIND, 128, 64, 3, 256>, args, 256, stream);
     case CFG_128_S5_R128:
       return launch<128, 128>((const void*)&gemm_v3<KIND, 128, 128, 5, 128>, args, 256, stream);

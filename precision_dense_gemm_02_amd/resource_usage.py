@@ -38,7 +38,8 @@ DEFAULT_KERNELS = {
     "lpgemm::gemm_v3<0, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "int8, 128x128 tiles (2048^3)",
     "lpgemm::gemm_v3<2, 128, 128, 4, 128, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "fp16, 128x128 tiles (2048^3)",
     "lpgemm::gemm_v3<1, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 1, false, false>": "int4, 128x128 tiles (2048^3), 32-byte fragment reads",
-    "lpgemm::gemm_v3<3, 128, 64, 3, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "dequant int8, M <= 128 (LLM M = 128)",
+    "lpgemm::gemm_v3<3, 128, 64, 3, 256, 5, false, false, 0, false, 0, false, false, false, 0, false, false>": "dequant int8, M <= 128 (LLM M = 128), B non-temporal",
+    "lpgemm::gemm_v3<0, 128, 64, 3, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, false>": "int8, 128x64 band tiles above 128 rows",
     "lpgemm::gemm_v3<0, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, true>": "int8 split-K (few tiles, long K)",
     "lpgemm::gemm_v3<1, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 1, false, true>": "int4 split-K",
     "lpgemm::gemm_v3<2, 128, 128, 2, 256, 0, false, false, 0, false, 0, false, false, false, 0, false, true>": "fp16 split-K",

@@ -2266,8 +2266,10 @@ __device__ __forceinline__ float wave_max(float v) {
 // and from HBM (graph-timed, one MI355X, weights cold: LLM M = 16 12.88
 // against 14.03 us, fp16 16 x 14336 x 4096 21.75 against 23.93, int8
 // 32 x 8192 x 8192 16.31 against 17.35); re-read from the Infinity Cache
-// call after call they gain or lose a few percent (-9% to +6%).  The
-// eight-wave kernel keeps the default: warm, it lost 11-25% with them.
+// call after call they gain or lose a few percent (-9% to +6%).  The fused
+// W8A8 kernel streams them non-temporally too (31.3 against 34.8 us cold,
+// 29.9 against 32.0 warm).  The eight-wave kernel keeps the default: warm,
+// it lost 11-25% with them.
 //
 // NB, p.tile_w: a workgroup holds NB 32-row blocks of B and owns p.tile_w
 // (at most 32 NB) columns of C from column p.tile_w * (its tile column) on;

@@ -439,7 +439,7 @@ lpgemm_status lpgemm_w8a8_fused(int64_t M, int64_t N, int64_t K, const void* X, 
   args.N = (int)N;
   args.row_bytes = (int)K;   // of the int8 operand; the binary16 rows are twice as long
   args.k_stages = (int)((K + 127) / 128);
-  return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND_I8_DEQUANT, 4, 1, true>, args, 256, stream);
+  return launch<32, 32>((const void*)&gemm_skinny_pipe<KIND_I8_DEQUANT, 4, 1, true, 1, 1>, args, 256, stream);
 }
 
 lpgemm_status lpgemm_quantize_rows_f16(int64_t M, int64_t K, const void* X, int8_t* Q,
